@@ -1,0 +1,216 @@
+"""Oracle block allocator (plain Python; test infrastructure only).
+
+What it models
+--------------
+* A pool of ``num_blocks`` physical KV blocks of ``block_size`` token slots
+  each, owned by the runtime, any of which can hold any logical block
+  [P1 "Paged Attention", body: the runtime owns a pool of physical blocks;
+  P3 "What is paged attention in vLLM...", Step 2: a free block fits any
+  request].
+* A free list and a reference count per block, kept beside the per-sequence
+  block tables [P3, Step 3: the block manager keeps the table next to a pool
+  of free blocks and one reference count per block].
+* A block table per sequence: logical block index (token order) -> physical
+  block id.  Token position ``pos`` lives in logical block ``pos // bs`` at
+  offset ``pos % bs`` [P1, body: the kernel derives logical block and offset
+  and looks up the physical id].  The filled-slot count of each table entry
+  is not stored; it follows from the sequence's token count.
+* Lazy allocation: a block is taken only when a token arrives and the last
+  block is full, never for a reserved maximum [P3, Step 4; P2 "PagedAttention
+  — AI Glossary", How it works, item 2].
+* Free on finish: every block whose count drops to zero returns to the free
+  pool and can be taken by the next request at once [P3, Step 4].
+* Prefix sharing by reference count: a fork points the child's table at the
+  parent's physical blocks and raises their counts [P2, How it works,
+  item 4; P3, Trade-offs and edge cases, third point].
+* Copy-on-write: when a sequence is about to write into a block that other
+  sequences still point at, only that block is duplicated; the writer's
+  table is redirected to the copy and the (source, destination) pair is
+  reported so the caller can copy the bytes [P2, How it works, item 5;
+  P3, Trade-offs, third point].
+
+Readings adopted where the pages are silent (stated once, used everywhere):
+
+* The free list is a LIFO stack.  ``free_order`` (a permutation of the block
+  ids, default ascending) is the order in which a fresh allocator hands
+  blocks out.  Freeing pushes a sequence's blocks in reverse logical order,
+  so its logical block 0 is handed out first afterwards.
+* Copy-on-write fires iff the block about to be written is a partially
+  filled tail whose count is above one.  Sequences are processed in call
+  order, so the last remaining sharer writes in place.
+* A slot is ``physical_block * block_size + offset``.
+* A call that runs out of blocks changes nothing (all-or-nothing over the
+  whole call) and raises ``OutOfBlocks``; the policy for that case belongs
+  to the caller [P1, FAQ "What happens when the GPU runs out of KV blocks?"].
+"""
+
+from __future__ import annotations
+
+import copy
+
+
+class AllocatorError(Exception):
+    """Base class; ``status`` names the C-ABI status the condition maps to."""
+
+    status = "ERROR"
+
+
+class InvalidArgument(AllocatorError):
+    status = "INVALID_ARGUMENT"
+
+
+class OutOfBlocks(AllocatorError):
+    status = "OUT_OF_BLOCKS"
+
+
+class UnknownSeq(AllocatorError):
+    status = "UNKNOWN_SEQ"
+
+
+class BlockAllocator:
+    """Free stack + reference counts + per-sequence tables."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks < 1 or block_size < 1:
+            raise InvalidArgument("num_blocks and block_size must be >= 1")
+        order = list(range(num_blocks)) if free_order is None else [int(x) for x in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise InvalidArgument("free_order must be a permutation of 0..num_blocks-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        # Stack with its top at the end: the first block handed out is order[0].
+        self._free = list(reversed(order))
+        self._rc = [0] * num_blocks
+        self._table: dict[int, list[int]] = {}
+        self._ntok: dict[int, int] = {}
+
+    # ------------------------------------------------------------------ state
+    def num_free(self) -> int:
+        return len(self._free)
+
+    def free_list(self) -> list[int]:
+        """Free blocks, the one handed out next first."""
+        return list(reversed(self._free))
+
+    def refcount(self, block: int) -> int:
+        if not 0 <= block < self.num_blocks:
+            raise InvalidArgument("block id out of range")
+        return self._rc[block]
+
+    def seq_block_table(self, seq_id: int) -> list[int]:
+        self._need(seq_id)
+        return list(self._table[seq_id])
+
+    def seq_num_tokens(self, seq_id: int) -> int:
+        self._need(seq_id)
+        return self._ntok[seq_id]
+
+    def seq_ids(self) -> list[int]:
+        return sorted(self._table)
+
+    # -------------------------------------------------------------- sequences
+    def seq_create(self, seq_id: int) -> None:
+        if seq_id in self._table:
+            raise InvalidArgument("sequence exists")
+        self._table[seq_id] = []
+        self._ntok[seq_id] = 0
+
+    def seq_fork(self, parent: int, child: int) -> None:
+        """Child shares every physical block of the parent (count + 1 each)."""
+        self._need(parent)
+        if child in self._table:
+            raise InvalidArgument("child exists")
+        self._table[child] = list(self._table[parent])
+        self._ntok[child] = self._ntok[parent]
+        for blk in self._table[child]:
+            self._rc[blk] += 1
+
+    def seq_free(self, seq_id: int) -> None:
+        """Drop one reference to each block; zero-count blocks rejoin the pool."""
+        self._need(seq_id)
+        for blk in reversed(self._table[seq_id]):
+            self._rc[blk] -= 1
+            if self._rc[blk] == 0:
+                self._free.append(blk)
+        del self._table[seq_id]
+        del self._ntok[seq_id]
+
+    def seq_reserve(self, seq_ids, n_new, cow_cap=None):
+        """Give ``n_new[i]`` new token slots to ``seq_ids[i]``, in call order.
+
+        Returns ``(slot_mapping, cow_pairs)``: one slot per new token,
+        sequence-major, and the (source, destination) block pairs whose
+        bytes must be copied before the new tokens are written.
+        """
+        seq_ids = [int(s) for s in seq_ids]
+        n_new = [int(n) for n in n_new]
+        if len(seq_ids) != len(n_new):
+            raise InvalidArgument("length mismatch")
+        seen = set()
+        for sid, n in zip(seq_ids, n_new):
+            if n < 0:
+                raise InvalidArgument("negative token count")
+            if sid not in self._table:
+                raise UnknownSeq(f"unknown sequence {sid}")
+            if sid in seen:
+                raise InvalidArgument("sequence listed twice")
+            seen.add(sid)
+
+        saved = (list(self._free), list(self._rc),
+                 copy.deepcopy(self._table), dict(self._ntok))
+        try:
+            slots, pairs = self._reserve(seq_ids, n_new)
+            if cow_cap is not None and len(pairs) > cow_cap:
+                raise InvalidArgument("copy-on-write pair capacity too small")
+        except AllocatorError:
+            self._free, self._rc, self._table, self._ntok = saved
+            raise
+        return slots, pairs
+
+    def block_tables(self, seq_ids, max_blocks: int):
+        """Rows of physical ids padded with -1, plus each sequence's length."""
+        rows, lens = [], []
+        for sid in seq_ids:
+            sid = int(sid)
+            self._need(sid)
+            tab = self._table[sid]
+            if len(tab) > max_blocks:
+                raise InvalidArgument("table longer than max_blocks")
+            rows.append(tab + [-1] * (max_blocks - len(tab)))
+            lens.append(self._ntok[sid])
+        return rows, lens
+
+    # ---------------------------------------------------------------- private
+    def _need(self, seq_id: int) -> None:
+        if seq_id not in self._table:
+            raise UnknownSeq(f"unknown sequence {seq_id}")
+
+    def _pop(self) -> int:
+        if not self._free:
+            raise OutOfBlocks("no free block")
+        return self._free.pop()
+
+    def _reserve(self, seq_ids, n_new):
+        bs = self.block_size
+        slots, pairs = [], []
+        for sid, n in zip(seq_ids, n_new):
+            table = self._table[sid]
+            for _ in range(n):
+                pos = self._ntok[sid]
+                lb, off = divmod(pos, bs)
+                if off == 0:
+                    # The last block is full (or there is none): take a block.
+                    blk = self._pop()
+                    self._rc[blk] = 1
+                    table.append(blk)
+                elif self._rc[table[lb]] > 1:
+                    # Writing into a block others still read: copy it first.
+                    src = table[lb]
+                    dst = self._pop()
+                    self._rc[src] -= 1
+                    self._rc[dst] = 1
+                    table[lb] = dst
+                    pairs.append((src, dst))
+                slots.append(table[lb] * bs + off)
+                self._ntok[sid] = pos + 1
+        return slots, pairs

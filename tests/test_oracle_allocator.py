@@ -1,0 +1,160 @@
+"""Oracle allocator and cache writes: invariants and workload-level pins."""
+
+import numpy as np
+import pytest
+from hypothesis import settings, strategies as st
+from hypothesis.stateful import RuleBasedStateMachine, invariant, precondition, rule
+
+import oracle_pins as pins
+import workloads as W
+from oracle import cache_ops as oc
+from oracle.allocator import BlockAllocator, InvalidArgument, OutOfBlocks, UnknownSeq
+from oracle_driver import OracleCache
+
+
+def test_append_and_copy_pins():
+    pins.check_append_places_rows(oc.cache_append)
+    pins.check_copy_whole_block(oc.copy_blocks)
+
+
+def test_append_rejects_duplicate_slot():
+    kc = np.zeros((2, 1, 2, 1), np.float32)
+    with pytest.raises(ValueError):
+        oc.cache_append(kc, kc.copy(), np.ones((2, 1, 1), np.float32),
+                        np.ones((2, 1, 1), np.float32), [1, 1], 2)
+
+
+def test_argument_errors():
+    with pytest.raises(InvalidArgument):
+        BlockAllocator(4, 4, [0, 1, 2, 2])
+    a = BlockAllocator(4, 4)
+    a.seq_create(1)
+    with pytest.raises(InvalidArgument):
+        a.seq_create(1)
+    with pytest.raises(UnknownSeq):
+        a.seq_reserve([2], [1])
+    with pytest.raises(InvalidArgument):
+        a.seq_reserve([1, 1], [1, 1])
+    with pytest.raises(InvalidArgument):
+        a.seq_reserve([1], [-1])
+    with pytest.raises(UnknownSeq):
+        a.seq_fork(5, 6)
+    with pytest.raises(InvalidArgument):
+        a.seq_fork(1, 1)
+    with pytest.raises(UnknownSeq):
+        a.seq_free(9)
+    a.seq_reserve([1], [5])
+    with pytest.raises(InvalidArgument):
+        a.block_tables([1], 1)
+
+
+def test_round_trip_through_table():
+    """Gathering a sequence's rows back through its table returns what was
+    appended, in logical order."""
+    w = W.tiny_ref()
+    c = OracleCache(w).run()
+    for b in w.seq_ids:
+        tab = c.alloc.seq_block_table(b)
+        L = c.alloc.seq_num_tokens(b)
+        got = np.stack([c.k_cache[tab[p // w.block_size], :, p % w.block_size] for p in range(L)])
+        assert np.array_equal(got, w.k_rows[w.logical_rows[b]])
+
+
+def test_prefix_sharing_copy_on_write_counts():
+    """Diverging from a prefix that ends half way into a block copies that
+    block for every sharer but the last; a block-aligned prefix copies none."""
+    w = W.prefix_sharing(batch=6, prefix_len=40, max_suffix=5)
+    c = OracleCache(w).run()
+    pairs = c.log[-1][1][1]
+    assert len(pairs) == 5
+    srcs = set(pairs[:, 0].tolist())
+    assert len(srcs) == 1  # the one shared tail block
+    w0 = W.prefix_sharing(batch=6, prefix_len=48, max_suffix=5)
+    c0 = OracleCache(w0).run()
+    assert len(c0.log[-1][1][1]) == 0
+    # Writing the children's copies never touched the parent's bits
+    # beyond its own new tokens, and every sequence still reads its own
+    # logical rows back.
+    for cc, ww in ((c, w), (c0, w0)):
+        for b in ww.seq_ids:
+            tab = cc.alloc.seq_block_table(b)
+            L = cc.alloc.seq_num_tokens(b)
+            got = np.stack([cc.v_cache[tab[p // 16], :, p % 16] for p in range(L)])
+            assert np.array_equal(got, ww.v_rows[ww.logical_rows[b]])
+
+
+def test_full_prefix_workload_pair_count():
+    w = W.prefix_sharing()
+    a = BlockAllocator(w.num_blocks, w.block_size, w.free_order)
+    for op in w.script[:-1]:
+        if op[0] == "create":
+            a.seq_create(op[1])
+        elif op[0] == "fork":
+            a.seq_fork(op[1], op[2])
+        else:
+            a.seq_reserve(op[1], op[2])
+    assert all(a.refcount(x) == 128 for x in a.seq_block_table(0))
+    slots, pairs = a.seq_reserve(w.script[-1][1], w.script[-1][2])
+    assert len(pairs) == 127
+    held = w.num_blocks - a.num_free()
+    assert held == w.notes["held_blocks"]
+
+
+class AllocatorMachine(RuleBasedStateMachine):
+    """Random create / fork / reserve / free sequences keep the invariants."""
+
+    def __init__(self):
+        super().__init__()
+        self.a = BlockAllocator(24, 4, list(np.random.default_rng(0).permutation(24)))
+        self.next_id = 0
+
+    @rule()
+    def create(self):
+        self.a.seq_create(self.next_id)
+        self.next_id += 1
+
+    @precondition(lambda self: self.a.seq_ids())
+    @rule(data=st.data())
+    def fork(self, data):
+        p = data.draw(st.sampled_from(self.a.seq_ids()))
+        self.a.seq_fork(p, self.next_id)
+        self.next_id += 1
+
+    @precondition(lambda self: self.a.seq_ids())
+    @rule(data=st.data())
+    def reserve(self, data):
+        ids = data.draw(st.lists(st.sampled_from(self.a.seq_ids()), min_size=1, max_size=4,
+                                 unique=True))
+        ns = [data.draw(st.integers(0, 7)) for _ in ids]
+        snap = self._snap()
+        try:
+            self.a.seq_reserve(ids, ns)
+        except OutOfBlocks:
+            assert self._snap() == snap
+
+    @precondition(lambda self: self.a.seq_ids())
+    @rule(data=st.data())
+    def free(self, data):
+        self.a.seq_free(data.draw(st.sampled_from(self.a.seq_ids())))
+
+    def _snap(self):
+        return (self.a.free_list(), [self.a.refcount(b) for b in range(24)],
+                {s: (self.a.seq_block_table(s), self.a.seq_num_tokens(s)) for s in self.a.seq_ids()})
+
+    @invariant()
+    def counts_match_tables(self):
+        rc = [self.a.refcount(b) for b in range(24)]
+        tabs = [self.a.seq_block_table(s) for s in self.a.seq_ids()]
+        assert sum(rc) == sum(len(t) for t in tabs)
+        for b in range(24):
+            assert rc[b] == sum(t.count(b) for t in tabs)
+        free = self.a.free_list()
+        assert len(set(free)) == len(free)
+        assert set(free) == {b for b in range(24) if rc[b] == 0}
+        for s in self.a.seq_ids():
+            n, t = self.a.seq_num_tokens(s), self.a.seq_block_table(s)
+            assert len(t) == -(-n // 4)
+
+
+TestAllocatorMachine = AllocatorMachine.TestCase
+TestAllocatorMachine.settings = settings(max_examples=60, stateful_step_count=30, deadline=None)
