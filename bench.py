@@ -1,0 +1,262 @@
+"""Benchmark of the paged-KV decode hot path on one MI355X.
+
+Workload (default): the Llama-3-8B attention shape at decode - 32 query / 8
+KV heads, head size 128, bf16 values, 16-token blocks - for the eight-request
+batch of the worked example on the clozo.ai page (lengths 128, 700, 1500,
+300, 2900, 50, 4100, 900), blocks drawn from a shuffled 4,096-block pool.
+
+One timed step is one decode step of the whole model's attention path:
+  * host: the C++ allocator reserves one new token per sequence (lazy block
+    allocation, copy-on-write pairs if any) and rebuilds the block tables;
+  * the slot mapping / tables / lengths go to the device (pinned, async);
+  * for each of the 32 layers (each with its own K/V pool, so the step reads
+    1.4 GB and cannot be served from the 256 MB last-level cache):
+    pa_copy_blocks (only if the allocator reported pairs), pa_cache_append of
+    the new token's K/V, pa_decode.
+Lengths grow by one token per step, as in real decoding; the KV bytes of
+every step are counted exactly.
+
+Reported: value = KV bytes read by pa_decode per second over the timed steps
+(GB/s, whole step, all host work included).  roofline: pa_decode alone,
+timed with HIP events around back-to-back launches over the 32 layer pools
+at the batch's exact lengths, against the 8 TB/s HBM peak.  cpu_baseline:
+the CPU oracle's paged decode on the same batch (one layer), timed on this
+host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention µs/step + KV-read GB/s (% of HBM peak), Llama-3-8B shape"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--kernel-reps", type=int, default=10,
+                   help="passes over the layer pools for the pa_decode roofline timing")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def to_dev(a, dtype, device):
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+def kv_bytes_per_token(w):
+    return 2 * w.num_kv_heads * w.head_dim * (2 if w.dtype == "bf16" else 4)
+
+
+def cpu_baseline(w, seconds):
+    """The oracle (NumPy fp64) on one layer of the same batch."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import allocator as oa
+    from oracle import attention as oatt
+    from oracle import cache_ops as oc
+
+    cores = len(os.sched_getaffinity(0))
+    alloc = oa.BlockAllocator(w.num_blocks, w.block_size, w.free_order)
+    kc, vc = w.empty_pool(), w.empty_pool()
+    for op in w.script:
+        if op[0] == "create":
+            alloc.seq_create(op[1])
+        else:
+            slots, _ = alloc.seq_reserve(op[1], op[2])
+            oc.cache_append(kc, vc, w.k_rows[op[3]], w.v_rows[op[3]], slots, w.block_size)
+    maxb = max(len(alloc.seq_block_table(s)) for s in w.seq_ids)
+    rows, lens = alloc.block_tables(w.seq_ids, maxb)
+    tables = np.array(rows, np.int32)
+    lens = np.array(lens, np.int32)
+    runs, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while True:
+            oatt.paged_decode(w.q, kc, vc, tables, lens, w.block_size, w.scale, w.dtype)
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    per = el / runs
+    gbs = int(lens.sum()) * kv_bytes_per_token(w) / per / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "us_per_layer": round(per * 1e6, 1),
+            "sample": f"{runs} full passes of one layer of the batch ({int(lens.sum())} tokens) "
+                      f"in {el:.1f} s, NumPy fp64 paged decode incl. bf16 widening"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path "
+              "shards by sequence or KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_338_amd as pa
+    import workloads as W
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = W.llama3_8b_decode()
+    B, L0 = w.batch, w.context_lens.copy()
+    H_q, H_kv, D, bs = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    nl = args.layers
+    total_steps = args.warmup + args.steps
+    maxb = int(math.ceil((L0.max() + total_steps + 1) / bs))
+    log(f"workload {w.name}: B={B} tokens={int(L0.sum())} layers={nl} pool={w.num_blocks} "
+        f"blocks/layer, maxb={maxb}")
+
+    # ---- set-up (untimed): allocator + prefill of every layer's pools
+    alloc = pa.Allocator(w.num_blocks, bs, w.free_order)
+    kpool = [to_dev(w.empty_pool(), w.dtype, dev) for _ in range(nl)]
+    vpool = [to_dev(w.empty_pool(), w.dtype, dev) for _ in range(nl)]
+    krows = to_dev(w.k_rows, w.dtype, dev)
+    vrows = to_dev(w.v_rows, w.dtype, dev)
+    for op in w.script:
+        if op[0] == "create":
+            alloc.seq_create(op[1])
+            continue
+        slots, pairs = alloc.seq_reserve(op[1], op[2])
+        assert len(pairs) == 0
+        idx = torch.from_numpy(op[3]).to(dev)
+        kr, vr = krows.index_select(0, idx), vrows.index_select(0, idx)
+        sd = torch.from_numpy(slots.copy()).to(dev)
+        for l in range(nl):
+            pa.pa_cache_append(kr, vr, sd, kpool[l], vpool[l])
+    del krows, vrows
+    q = to_dev(w.q, w.dtype, dev)
+    outs = [torch.empty_like(q) for _ in range(nl)]
+    ws = pa.decode_workspace(kpool[0], B, H_q, maxb)
+    tables_np, lens_np = alloc.build_block_tables(w.seq_ids, maxb)
+    tables_d = torch.from_numpy(tables_np).to(dev)
+    lens_d = torch.from_numpy(lens_np).to(dev)
+    torch.cuda.synchronize()
+    log("prefill done")
+
+    # ---- roofline leg: pa_decode alone, back-to-back over the layer pools
+    stream = torch.cuda.current_stream()
+    dec = [pa.prepare_decode(q, kpool[l], vpool[l], tables_d, lens_d, bs, w.scale, outs[l], ws)
+           for l in range(nl)]
+    for l in range(nl):
+        dec[l]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.kernel_reps):
+        for l in range(nl):
+            dec[l]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    launches = args.kernel_reps * nl
+    us_launch = e0.elapsed_time(e1) * 1e3 / launches
+    kv_launch = int(lens_np.sum()) * kv_bytes_per_token(w)
+    achieved = kv_launch / (us_launch * 1e-6) / 1e9
+    log(f"pa_decode: {us_launch:.2f} us/launch, {achieved:.0f} GB/s over {launches} launches")
+
+    # ---- whole decode steps
+    new_k = to_dev(w.notes["new_k"], w.dtype, dev)
+    new_v = to_dev(w.notes["new_v"], w.dtype, dev)
+    pin = [dict(slots=torch.empty(B, dtype=torch.int64, pin_memory=True),
+                tables=torch.empty((B, maxb), dtype=torch.int32, pin_memory=True),
+                lens=torch.empty(B, dtype=torch.int32, pin_memory=True),
+                pairs=torch.empty((B, 2), dtype=torch.int32, pin_memory=True),
+                ev=torch.cuda.Event()) for _ in range(2)]
+    slots_d = torch.empty(B, dtype=torch.int64, device=dev)
+    pairs_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
+    app = [pa.prepare_cache_append(new_k, new_v, slots_d, kpool[l], vpool[l]) for l in range(nl)]
+    seq_ids = np.array(w.seq_ids, np.int64)
+    ones = np.ones(B, np.int32)
+    kv_read = []
+
+    def step(i):
+        buf = pin[i % 2]
+        buf["ev"].synchronize()  # its previous upload has finished
+        slots_np = buf["slots"].numpy()
+        s, p = alloc.seq_reserve(seq_ids, ones, cow_cap=B, out=slots_np)
+        npairs = len(p)
+        if npairs:
+            buf["pairs"].numpy()[:npairs] = p
+        alloc.build_block_tables(seq_ids, maxb, tables_out=buf["tables"].numpy(),
+                                 lens_out=buf["lens"].numpy())
+        slots_d.copy_(buf["slots"], non_blocking=True)
+        tables_d.copy_(buf["tables"], non_blocking=True)
+        lens_d.copy_(buf["lens"], non_blocking=True)
+        if npairs:
+            pairs_d[:npairs].copy_(buf["pairs"][:npairs], non_blocking=True)
+        buf["ev"].record(stream)
+        kv_read.append(int(buf["lens"].numpy().sum()) * kv_bytes_per_token(w) * nl)
+        for l in range(nl):
+            if npairs:
+                pa.prepare_copy_blocks(pairs_d, npairs, kpool[l], vpool[l])()
+            app[l]()
+            dec[l]()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    kv_read.clear()
+    t_start = time.perf_counter()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for i in range(args.warmup, total_steps):
+        step(i)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = s0.elapsed_time(s1)
+    ms_step = max(gpu_ms, wall * 1e3) / args.steps
+    value = sum(kv_read) / (ms_step * args.steps * 1e-3) / 1e9
+    log(f"steps: {ms_step:.3f} ms/step ({ms_step * 1e3 / nl:.2f} us/layer), {value:.0f} GB/s")
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_decode: per step, host slot reservation + table upload, "
+                               f"then {nl} layers x (pa_cache_append + pa_decode); 32 Q / 8 KV "
+                               "heads, head 128, bs 16, bf16, pool 4096 blocks per layer",
+                   "batch": B, "context_lens_at_first_step": (L0 + args.warmup + 1).tolist(),
+                   "tokens_added_per_step": B, "layers": nl,
+                   "us_per_layer": round(ms_step * 1e3 / nl, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_decode (split + merge kernels), one layer, "
+                               f"{int(lens_np.sum())} tokens x 4096 B",
+                     "us_per_launch": round(us_launch, 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)...")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

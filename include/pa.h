@@ -1,0 +1,223 @@
+/*
+ * pa.h - C ABI of the paged KV cache library (gfx950 / MI355X).
+ *
+ * The library implements the hot path of a paged KV cache for LLM decode:
+ * K and V live in fixed-size blocks scattered through a physical pool, and a
+ * per-sequence block table maps each logical token position to
+ * (logical block, offset) and then to a physical block id.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [P1] "Paged Attention", klaylearn.com glossary
+ *   [P2] "PagedAttention - AI Glossary", modelrefs.com
+ *   [P3] "What is paged attention in vLLM, and why does it matter?",
+ *        interview.clozo.ai blog
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every call returns a pa_status and never throws.  On an error the
+ *   thread-local text from pa_last_error() says what was wrong.
+ * - Device operations take DEVICE pointers owned by the caller (the library
+ *   never allocates or frees device memory) and a hipStream_t passed as
+ *   void*.  They only enqueue work on that stream and return; ordering
+ *   between them (copy, then append, then decode) is the caller's stream
+ *   order.  Host-checkable arguments are validated before anything is
+ *   enqueued; a rejected call enqueues nothing.  Kernel launch failures come
+ *   back as PA_ERR_DEVICE.
+ * - Contents of device arrays (slots, table entries, lengths, pairs) are
+ *   preconditions the host cannot check without a copy.  The kernels never
+ *   touch memory outside the buffers described here: slots or block ids
+ *   outside the pool are skipped (append, copy) or clamped into it (decode,
+ *   whose output for such a sequence is then unspecified), and lengths are
+ *   clamped to max_blocks_per_seq * block_size.
+ * - KV pool layout: two pools, k_cache and v_cache, each
+ *   [num_blocks][num_kv_heads][block_size][head_dim], row-major, values of
+ *   the pool's dtype.  One (block, KV head) tile is contiguous.
+ * - Slot of a token: physical_block * block_size + offset_in_block, int64.
+ * - Block tables: int32 [num_seqs][max_blocks_per_seq], row b lists the
+ *   physical blocks of sequence b in logical (token) order; entries past
+ *   ceil(context_len / block_size) are never read (pad with -1).
+ * - Host allocator handles are not thread-safe; use one per thread or lock.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef int32_t pa_status;
+#define PA_OK 0
+#define PA_ERR_INVALID_ARGUMENT 1
+#define PA_ERR_OUT_OF_BLOCKS 2
+#define PA_ERR_UNKNOWN_SEQ 3
+#define PA_ERR_UNSUPPORTED 4
+#define PA_ERR_DEVICE 5
+
+typedef int32_t pa_dtype;
+#define PA_F32 0
+#define PA_BF16 1
+
+/* Shape of one KV pool pair.  Supported: block_size a power of two in
+ * [1, 256]; head_dim 64 or 128; dtype PA_F32 or PA_BF16. */
+typedef struct pa_cache_desc {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  pa_dtype dtype;
+} pa_cache_desc;
+
+/* Version of this header the library was built from (PA_ABI_VERSION). */
+int32_t pa_abi_version(void);
+
+/* Static name of a status code ("PA_OK", ...); "PA_UNKNOWN_STATUS" else. */
+const char* pa_status_string(pa_status status);
+
+/* Detail of the last error raised on the calling thread ("" if none).  The
+ * pointer stays valid until the thread's next library call. */
+const char* pa_last_error(void);
+
+/* PA_OK if the library has kernels for this pool shape and query-head count
+ * (num_q_heads a multiple of num_kv_heads, group size num_q_heads /
+ * num_kv_heads in [1, 16]); PA_ERR_UNSUPPORTED or PA_ERR_INVALID_ARGUMENT
+ * otherwise. */
+pa_status pa_supported(const pa_cache_desc* desc, int32_t num_q_heads);
+
+/* ---------------------------------------------------------------- device */
+
+/* Slot-mapped append [P3 Step 4: each decode step writes the new token's
+ * keys and values into the last block; P1 body: prefill fills the blocks of
+ * the prompt the same way].
+ *
+ * For every t < num_tokens with slot = slot_mapping[t] >= 0:
+ *   k_cache[slot / bs][h][slot % bs][:] = k[t][h][:]   for every KV head h
+ *   v_cache[...]                        = v[t][h][:]
+ * k, v:          device, [num_tokens][num_kv_heads][head_dim], pool dtype.
+ * slot_mapping:  device int64 [num_tokens]; negative = skip (padding);
+ *                non-negative slots must be distinct within one call.
+ * Exact bit copy.  num_tokens == 0 enqueues nothing. */
+pa_status pa_cache_append(const void* k, const void* v, const int64_t* slot_mapping,
+                          int32_t num_tokens, void* k_cache, void* v_cache,
+                          const pa_cache_desc* desc, void* stream);
+
+/* Whole-block copy for copy-on-write [P2 How it works, item 5: only the
+ * block being written is copied; P3 Trade-offs, third point].
+ *
+ * For every pair i < num_pairs: block dst = src_dst_pairs[2i+1] of both pools
+ * becomes a bit copy of block src = src_dst_pairs[2i] (all heads, all slots).
+ * src_dst_pairs: device int32 [num_pairs][2].  Destinations must be
+ * distinct and must not appear as sources.  num_pairs == 0 enqueues
+ * nothing. */
+pa_status pa_copy_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, void* k_cache,
+                         void* v_cache, const pa_cache_desc* desc, void* stream);
+
+/* Single-query (decode) attention through the block tables [P1 body: the
+ * kernel derives each token's logical block and offset, looks up the
+ * physical block and reads K/V there without first gathering the sequence;
+ * P3 Step 3; P2 Example: the attention arithmetic is unchanged].
+ *
+ * For every sequence b < num_seqs and query head h < num_q_heads, with
+ * G = num_q_heads / num_kv_heads, kvh = h / G, L = context_lens[b]:
+ *   s_p      = scale * dot(q[b][h], K(b, p, kvh))          for p < L
+ *   out[b][h] = sum_p softmax(s)_p * V(b, p, kvh)
+ * where K(b, p, kvh) = k_cache[block_tables[b][p / bs]][kvh][p % bs][:].
+ * L == 0 gives a zero row.  Arithmetic in fp32, one rounding to the output
+ * dtype (= pool dtype).
+ * q:            device [num_seqs][num_q_heads][head_dim], pool dtype.
+ * block_tables: device int32 [num_seqs][max_blocks_per_seq].
+ * context_lens: device int32 [num_seqs].
+ * block_size:   must equal desc->block_size.
+ * out:          device [num_seqs][num_q_heads][head_dim], pool dtype.
+ * workspace:    device scratch of at least pa_decode_workspace_size() bytes,
+ *               256-byte aligned; the call owns it until the stream reaches
+ *               the end of the call. */
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                    float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode needs for this shape (independent of the
+ * lengths' values). */
+pa_status pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                   size_t* bytes);
+
+/* ------------------------------------------------------------ allocator */
+
+/* Host block allocator: a free list, one reference count per block and one
+ * block table per sequence [P3 Step 3: the block manager keeps the tables
+ * beside a pool of free blocks and per-block reference counts].
+ *
+ * - Lazy allocation: a sequence takes a block only when a token arrives and
+ *   its last block is full [P3 Step 4; P2 How it works, item 2].
+ * - Free list: LIFO.  A fresh allocator hands blocks out in free_order
+ *   (a permutation of 0..num_blocks-1; NULL = ascending).  pa_seq_free
+ *   pushes a sequence's blocks in reverse logical order, so its logical
+ *   block 0 is handed out first afterwards [P3 Step 4: freed blocks can be
+ *   taken by other requests at once].
+ * - Fork shares every block of the parent (count + 1) [P2 How it works,
+ *   item 4].
+ * - Copy-on-write: a token written into a partly filled block with count > 1
+ *   first moves the writer to a fresh block and reports (src, dst) for
+ *   pa_copy_blocks [P2 How it works, item 5].  Sequences are processed in
+ *   call order, so the last remaining sharer writes in place.  A full shared
+ *   block is never copied (the next token takes a fresh block).
+ * - Every call gives the strong guarantee: on any error nothing changed.
+ * Handles are owned by the caller (create/destroy); not thread-safe. */
+typedef struct pa_allocator pa_allocator;
+
+pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size,
+                              const int32_t* free_order /* host, nullable */,
+                              pa_allocator** out);
+void pa_allocator_destroy(pa_allocator* alloc);
+
+/* New empty sequence.  INVALID_ARGUMENT if the id exists. */
+pa_status pa_seq_create(pa_allocator* alloc, int64_t seq_id);
+
+/* child := copy of parent's table and length; each block's count + 1.
+ * UNKNOWN_SEQ if parent is absent, INVALID_ARGUMENT if child exists. */
+pa_status pa_seq_fork(pa_allocator* alloc, int64_t parent, int64_t child);
+
+/* Gives n_new[i] new tokens to seq_ids[i] for i < n, in that order.
+ * slot_mapping_out: host int64 [sum(n_new)], sequence-major in call order.
+ * cow_pairs_out:    host int32 [cow_cap][2] (src, dst); *num_cow_out = count.
+ * Errors (checked in order for each i before any change): n_new[i] < 0 or a
+ * repeated id -> INVALID_ARGUMENT; unknown id -> UNKNOWN_SEQ.  Running out of
+ * blocks -> OUT_OF_BLOCKS, more pairs than cow_cap -> INVALID_ARGUMENT; both
+ * leave the allocator exactly as before the call (all-or-nothing). */
+pa_status pa_seq_reserve(pa_allocator* alloc, const int64_t* seq_ids, const int32_t* n_new,
+                         int32_t n, int64_t* slot_mapping_out, int32_t* cow_pairs_out,
+                         int32_t cow_cap, int32_t* num_cow_out);
+
+/* Drops the sequence; blocks whose count reaches zero rejoin the free list. */
+pa_status pa_seq_free(pa_allocator* alloc, int64_t seq_id);
+
+/* tables_out: host int32 [n][max_blocks_per_seq] padded with -1;
+ * context_lens_out: host int32 [n].  INVALID_ARGUMENT if a table is longer
+ * than max_blocks_per_seq, UNKNOWN_SEQ for an absent id. */
+pa_status pa_build_block_tables(const pa_allocator* alloc, const int64_t* seq_ids, int32_t n,
+                                int32_t max_blocks_per_seq, int32_t* tables_out,
+                                int32_t* context_lens_out);
+
+/* Snapshot getters (host memory). */
+int32_t pa_allocator_num_free(const pa_allocator* alloc);
+/* Free blocks, the one handed out next first; *len = count, at most cap
+ * written (INVALID_ARGUMENT if cap is too small, nothing written). */
+pa_status pa_allocator_free_list(const pa_allocator* alloc, int32_t* out, int32_t cap,
+                                 int32_t* len);
+pa_status pa_block_refcount(const pa_allocator* alloc, int32_t block, int32_t* out);
+pa_status pa_seq_block_table(const pa_allocator* alloc, int64_t seq_id, int32_t* out,
+                             int32_t cap, int32_t* len);
+pa_status pa_seq_num_tokens(const pa_allocator* alloc, int64_t seq_id, int32_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

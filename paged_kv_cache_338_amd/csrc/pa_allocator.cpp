@@ -1,0 +1,309 @@
+// Host block allocator: free stack, per-block reference counts and one block
+// table per sequence, with lazy allocation, fork and copy-on-write.
+//
+// Sources: "What is paged attention in vLLM, and why does it matter?"
+// (interview.clozo.ai), Step 3 (table + free pool + per-block counts) and
+// Step 4 (allocate only when the last block is full; blocks return to the
+// pool on finish); "PagedAttention - AI Glossary" (modelrefs.com), How it
+// works, items 2, 4 and 5 (grow block by block; shared prefixes by reference
+// count; copy only the block being written).
+//
+// Every entry point gives the strong guarantee: pa_seq_reserve keeps an undo
+// log while it walks the tokens and replays it backwards when it runs out of
+// blocks or out of room for copy pairs, so a failed call leaves the free
+// stack order, counts and tables exactly as they were.
+#include <algorithm>
+#include <cstdint>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+struct Sequence {
+  std::vector<int32_t> table;  // logical block -> physical block
+  int32_t num_tokens = 0;
+};
+
+// One reversible change made by a reserve call.
+struct Undo {
+  enum Kind : uint8_t { kPop, kRefcount, kTableAppend, kTableSet, kTokens } kind;
+  Sequence* seq;
+  int32_t a;  // block (kPop, kRefcount), logical index (kTableSet)
+  int32_t b;  // old value (kRefcount, kTableSet, kTokens)
+};
+
+}  // namespace
+
+struct pa_allocator {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // top at back()
+  std::vector<int32_t> refcount;
+  std::unordered_map<int64_t, Sequence> seqs;
+  std::vector<Undo> undo;  // reused between calls
+
+  Sequence* find(int64_t id) {
+    auto it = seqs.find(id);
+    return it == seqs.end() ? nullptr : &it->second;
+  }
+  const Sequence* find(int64_t id) const {
+    auto it = seqs.find(id);
+    return it == seqs.end() ? nullptr : &it->second;
+  }
+
+  void rollback() {
+    for (auto it = undo.rbegin(); it != undo.rend(); ++it) {
+      switch (it->kind) {
+        case Undo::kPop: free_stack.push_back(it->a); break;
+        case Undo::kRefcount: refcount[it->a] = it->b; break;
+        case Undo::kTableAppend: it->seq->table.pop_back(); break;
+        case Undo::kTableSet: it->seq->table[it->a] = it->b; break;
+        case Undo::kTokens: it->seq->num_tokens = it->b; break;
+      }
+    }
+    undo.clear();
+  }
+
+  bool pop(int32_t* blk) {
+    if (free_stack.empty()) return false;
+    *blk = free_stack.back();
+    free_stack.pop_back();
+    undo.push_back({Undo::kPop, nullptr, *blk, 0});
+    return true;
+  }
+
+  void set_refcount(int32_t blk, int32_t value) {
+    undo.push_back({Undo::kRefcount, nullptr, blk, refcount[blk]});
+    refcount[blk] = value;
+  }
+};
+
+extern "C" {
+
+pa_status pa_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                              pa_allocator** out) {
+  if (!out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (num_blocks < 1 || block_size < 1)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_blocks (%d) and block_size (%d) must be >= 1",
+                    num_blocks, block_size);
+  pa_allocator* a = new (std::nothrow) pa_allocator;
+  if (!a) return pa::fail(PA_ERR_INVALID_ARGUMENT, "host allocation failed");
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->refcount.assign(num_blocks, 0);
+  a->free_stack.resize(num_blocks);
+  if (free_order) {
+    std::vector<uint8_t> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t x = free_order[i];
+      if (x < 0 || x >= num_blocks || seen[x]) {
+        delete a;
+        return pa::fail(PA_ERR_INVALID_ARGUMENT,
+                        "free_order is not a permutation of 0..%d (entry %d = %d)",
+                        num_blocks - 1, i, x);
+      }
+      seen[x] = 1;
+    }
+  }
+  // The first block handed out is free_order[0]: it goes on top of the stack.
+  for (int32_t i = 0; i < num_blocks; ++i)
+    a->free_stack[num_blocks - 1 - i] = free_order ? free_order[i] : i;
+  *out = a;
+  return PA_OK;
+}
+
+void pa_allocator_destroy(pa_allocator* alloc) { delete alloc; }
+
+pa_status pa_seq_create(pa_allocator* alloc, int64_t seq_id) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  if (alloc->find(seq_id))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld exists", (long long)seq_id);
+  alloc->seqs.emplace(seq_id, Sequence{});
+  return PA_OK;
+}
+
+pa_status pa_seq_fork(pa_allocator* alloc, int64_t parent, int64_t child) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  const Sequence* p = alloc->find(parent);
+  if (!p) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown parent sequence %lld", (long long)parent);
+  if (alloc->find(child))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "child sequence %lld exists", (long long)child);
+  Sequence copy = *p;  // copy before emplace: emplace may rehash
+  for (int32_t blk : copy.table) alloc->refcount[blk] += 1;
+  alloc->seqs.emplace(child, std::move(copy));
+  return PA_OK;
+}
+
+pa_status pa_seq_free(pa_allocator* alloc, int64_t seq_id) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  auto it = alloc->seqs.find(seq_id);
+  if (it == alloc->seqs.end())
+    return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  const std::vector<int32_t>& t = it->second.table;
+  for (auto r = t.rbegin(); r != t.rend(); ++r) {
+    if (--alloc->refcount[*r] == 0) alloc->free_stack.push_back(*r);
+  }
+  alloc->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status pa_seq_reserve(pa_allocator* alloc, const int64_t* seq_ids, const int32_t* n_new,
+                         int32_t n, int64_t* slot_mapping_out, int32_t* cow_pairs_out,
+                         int32_t cow_cap, int32_t* num_cow_out) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  if (n < 0) return pa::fail(PA_ERR_INVALID_ARGUMENT, "n = %d < 0", n);
+  if (n > 0 && (!seq_ids || !n_new))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "seq_ids / n_new is NULL");
+  if (cow_cap < 0) return pa::fail(PA_ERR_INVALID_ARGUMENT, "cow_cap < 0");
+  if (cow_cap > 0 && !cow_pairs_out)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "cow_pairs_out is NULL with cow_cap > 0");
+
+  std::vector<Sequence*> seqs(n);
+  std::unordered_set<int64_t> seen;
+  seen.reserve(static_cast<size_t>(n) * 2);
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (n_new[i] < 0)
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "n_new[%d] = %d < 0", i, n_new[i]);
+    seqs[i] = alloc->find(seq_ids[i]);
+    if (!seqs[i])
+      return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if (!seen.insert(seq_ids[i]).second)
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld listed twice",
+                      (long long)seq_ids[i]);
+    if (static_cast<int64_t>(seqs[i]->num_tokens) + n_new[i] > INT32_MAX)
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld would exceed INT32_MAX tokens",
+                      (long long)seq_ids[i]);
+    total += n_new[i];
+  }
+  if (total > 0 && !slot_mapping_out)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "slot_mapping_out is NULL");
+
+  const int32_t bs = alloc->block_size;
+  alloc->undo.clear();
+  int32_t pairs = 0;
+  int64_t t = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Sequence* s = seqs[i];
+    if (n_new[i] == 0) continue;
+    alloc->undo.push_back({Undo::kTokens, s, 0, s->num_tokens});
+    for (int32_t j = 0; j < n_new[i]; ++j) {
+      const int32_t pos = s->num_tokens;
+      const int32_t lb = pos / bs, off = pos % bs;
+      if (off == 0) {
+        int32_t blk;
+        if (!alloc->pop(&blk)) {
+          alloc->rollback();
+          return pa::fail(PA_ERR_OUT_OF_BLOCKS, "no free block (pool of %d)", alloc->num_blocks);
+        }
+        alloc->set_refcount(blk, 1);
+        s->table.push_back(blk);
+        alloc->undo.push_back({Undo::kTableAppend, s, 0, 0});
+      } else if (alloc->refcount[s->table[lb]] > 1) {
+        const int32_t src = s->table[lb];
+        int32_t dst;
+        if (!alloc->pop(&dst)) {
+          alloc->rollback();
+          return pa::fail(PA_ERR_OUT_OF_BLOCKS, "no free block (pool of %d)", alloc->num_blocks);
+        }
+        alloc->set_refcount(src, alloc->refcount[src] - 1);
+        alloc->set_refcount(dst, 1);
+        alloc->undo.push_back({Undo::kTableSet, s, lb, src});
+        s->table[lb] = dst;
+        if (pairs < cow_cap) {
+          cow_pairs_out[2 * pairs] = src;
+          cow_pairs_out[2 * pairs + 1] = dst;
+        }
+        ++pairs;
+      }
+      slot_mapping_out[t++] = static_cast<int64_t>(s->table[lb]) * bs + off;
+      s->num_tokens = pos + 1;
+    }
+  }
+  if (pairs > cow_cap) {
+    // Checked after the walk so that running out of blocks is reported first.
+    alloc->rollback();
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "%d copy pairs > cow_cap = %d", pairs, cow_cap);
+  }
+  alloc->undo.clear();
+  if (num_cow_out) *num_cow_out = pairs;
+  return PA_OK;
+}
+
+pa_status pa_build_block_tables(const pa_allocator* alloc, const int64_t* seq_ids, int32_t n,
+                                int32_t max_blocks_per_seq, int32_t* tables_out,
+                                int32_t* context_lens_out) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  if (n < 0 || max_blocks_per_seq < 1)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "n = %d, max_blocks_per_seq = %d", n,
+                    max_blocks_per_seq);
+  if (n > 0 && (!seq_ids || !tables_out || !context_lens_out))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL array");
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence* s = alloc->find(seq_ids[i]);
+    if (!s) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if (static_cast<int64_t>(s->table.size()) > max_blocks_per_seq)
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld holds %zu blocks > %d",
+                      (long long)seq_ids[i], s->table.size(), max_blocks_per_seq);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence* s = alloc->find(seq_ids[i]);
+    int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks_per_seq;
+    std::copy(s->table.begin(), s->table.end(), row);
+    std::fill(row + s->table.size(), row + max_blocks_per_seq, -1);
+    context_lens_out[i] = s->num_tokens;
+  }
+  return PA_OK;
+}
+
+int32_t pa_allocator_num_free(const pa_allocator* alloc) {
+  return alloc ? static_cast<int32_t>(alloc->free_stack.size()) : -1;
+}
+
+pa_status pa_allocator_free_list(const pa_allocator* alloc, int32_t* out, int32_t cap,
+                                 int32_t* len) {
+  if (!alloc || !len) return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL argument");
+  const int32_t nf = static_cast<int32_t>(alloc->free_stack.size());
+  *len = nf;
+  if (cap < nf) return pa::fail(PA_ERR_INVALID_ARGUMENT, "cap %d < %d free blocks", cap, nf);
+  if (nf > 0 && !out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "out is NULL");
+  std::copy(alloc->free_stack.rbegin(), alloc->free_stack.rend(), out);
+  return PA_OK;
+}
+
+pa_status pa_block_refcount(const pa_allocator* alloc, int32_t block, int32_t* out) {
+  if (!alloc || !out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (block < 0 || block >= alloc->num_blocks)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "block %d outside 0..%d", block,
+                    alloc->num_blocks - 1);
+  *out = alloc->refcount[block];
+  return PA_OK;
+}
+
+pa_status pa_seq_block_table(const pa_allocator* alloc, int64_t seq_id, int32_t* out, int32_t cap,
+                             int32_t* len) {
+  if (!alloc || !len) return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL argument");
+  const Sequence* s = alloc->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  const int32_t nb = static_cast<int32_t>(s->table.size());
+  *len = nb;
+  if (cap < nb) return pa::fail(PA_ERR_INVALID_ARGUMENT, "cap %d < %d blocks", cap, nb);
+  if (nb > 0 && !out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "out is NULL");
+  std::copy(s->table.begin(), s->table.end(), out);
+  return PA_OK;
+}
+
+pa_status pa_seq_num_tokens(const pa_allocator* alloc, int64_t seq_id, int32_t* out) {
+  if (!alloc || !out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL argument");
+  const Sequence* s = alloc->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  *out = s->num_tokens;
+  return PA_OK;
+}
+
+}  // extern "C"

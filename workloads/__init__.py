@@ -20,7 +20,8 @@ Every workload is described by
   sequence b's tokens in logical order (what a contiguous cache would hold).
 
 Draw order within one workload: lengths, free_order, q, K, V (K and V
-sequence-major, logical order).  Pools start filled with NaN bit patterns so
+sequence-major, logical order).  ``with_values=False`` skips q/K/V (for
+allocator-only use); everything drawn before them is unchanged.  Pools start filled with NaN bit patterns so
 that a read of an unwritten slot shows up.
 """
 
@@ -43,7 +44,9 @@ def round_to_bf16_bits(x):
     return (rounded >> np.uint32(16)).astype(np.uint16)
 
 
-def _normal(rng, shape, dtype):
+def _normal(rng, shape, dtype, draw=True):
+    if not draw:
+        return None
     x = rng.standard_normal(size=shape, dtype=np.float32)
     return round_to_bf16_bits(x) if dtype == "bf16" else x
 
@@ -124,16 +127,16 @@ def _round_robin_script(lengths, block_size):
     return script, logical
 
 
-def tiny_ref(seed=1):
+def tiny_ref(seed=1, with_values=True):
     """4 sequences of 7/16/33/100 tokens, 4 Q / 2 KV heads, head 64, bs 4, fp32."""
     lengths = [7, 16, 33, 100]
     rng = np.random.default_rng(seed)
     nb, bs, hq, hkv, d = 64, 4, 4, 2, 64
     free_order = rng.permutation(nb).astype(np.int32)
-    q = _normal(rng, (len(lengths), hq, d), "f32")
+    q = _normal(rng, (len(lengths), hq, d), "f32", with_values)
     tot = sum(lengths)
-    k = _normal(rng, (tot, hkv, d), "f32")
-    v = _normal(rng, (tot, hkv, d), "f32")
+    k = _normal(rng, (tot, hkv, d), "f32", with_values)
+    v = _normal(rng, (tot, hkv, d), "f32", with_values)
     script, logical = _sequential_script(lengths)
     return Workload("tiny_ref", seed, hq, hkv, d, bs, "f32", 1.0 / 8.0, nb, free_order,
                     q, k, v, script, list(range(len(lengths))), logical)
@@ -142,7 +145,7 @@ def tiny_ref(seed=1):
 LLAMA3_8B_BATCH = [128, 700, 1500, 300, 2900, 50, 4100, 900]
 
 
-def llama3_8b_decode(seed=2, lengths=None, num_blocks=4096, block_size=16):
+def llama3_8b_decode(seed=2, lengths=None, num_blocks=4096, block_size=16, with_values=True):
     """One Llama-3-8B attention layer at decode: 32 Q / 8 KV heads, head 128.
 
     Default lengths are the eight-request batch of the worked example in
@@ -153,12 +156,12 @@ def llama3_8b_decode(seed=2, lengths=None, num_blocks=4096, block_size=16):
     rng = np.random.default_rng(seed)
     hq, hkv, d = 32, 8, 128
     free_order = rng.permutation(num_blocks).astype(np.int32)
-    q = _normal(rng, (len(lengths), hq, d), "bf16")
+    q = _normal(rng, (len(lengths), hq, d), "bf16", with_values)
     tot = sum(lengths)
-    k = _normal(rng, (tot, hkv, d), "bf16")
-    v = _normal(rng, (tot, hkv, d), "bf16")
-    new_k = _normal(rng, (len(lengths), hkv, d), "bf16")
-    new_v = _normal(rng, (len(lengths), hkv, d), "bf16")
+    k = _normal(rng, (tot, hkv, d), "bf16", with_values)
+    v = _normal(rng, (tot, hkv, d), "bf16", with_values)
+    new_k = _normal(rng, (len(lengths), hkv, d), "bf16", with_values)
+    new_v = _normal(rng, (len(lengths), hkv, d), "bf16", with_values)
     script, logical = _sequential_script(lengths)
     return Workload("llama3_8b_decode", seed, hq, hkv, d, block_size, "bf16",
                     1.0 / math.sqrt(d), num_blocks, free_order, q, k, v, script,
@@ -166,7 +169,7 @@ def llama3_8b_decode(seed=2, lengths=None, num_blocks=4096, block_size=16):
                     notes={"new_k": new_k, "new_v": new_v})
 
 
-def serving_batch(seed=3, batch=256):
+def serving_batch(seed=3, batch=256, with_values=True):
     """256 sequences, log-normal lengths (mean 600, sigma 1, capped at 8192),
     interleaved in a pool of ceil(1.1 * total / 16) blocks, then one appended
     token per sequence before the decode.
@@ -179,9 +182,9 @@ def serving_batch(seed=3, batch=256):
     nb = -(-(11 * total) // (10 * bs))
     assert nb >= sum(-(-(L + 1) // bs) for L in lengths)
     free_order = rng.permutation(nb).astype(np.int32)
-    q = _normal(rng, (batch, hq, d), "bf16")
-    k = _normal(rng, (total + batch, hkv, d), "bf16")
-    v = _normal(rng, (total + batch, hkv, d), "bf16")
+    q = _normal(rng, (batch, hq, d), "bf16", with_values)
+    k = _normal(rng, (total + batch, hkv, d), "bf16", with_values)
+    v = _normal(rng, (total + batch, hkv, d), "bf16", with_values)
     script, logical = _round_robin_script(lengths, bs)
     new_rows = np.arange(total, total + batch, dtype=np.int64)
     script.append(("reserve", list(range(batch)), [1] * batch, new_rows))
@@ -194,7 +197,7 @@ def serving_batch(seed=3, batch=256):
 BLOCK_SIZE_SWEEP = (8, 16, 32, 128)
 
 
-def block_size_sweep(block_size, seed=4, batch=64, max_len=8192):
+def block_size_sweep(block_size, seed=4, batch=64, max_len=8192, with_values=True):
     """64 sequences with lengths uniform on [1, 8192]; same lengths and values
     for every block size, pool ceil(1.1 * blocks needed), shuffled per size.
     """
@@ -206,17 +209,17 @@ def block_size_sweep(block_size, seed=4, batch=64, max_len=8192):
     needed = sum(-(-L // block_size) for L in lengths)
     nb = -(-(11 * needed) // 10)
     free_order = np.random.default_rng(seed * 1000 + block_size).permutation(nb).astype(np.int32)
-    q = _normal(rng, (batch, hq, d), "bf16")
+    q = _normal(rng, (batch, hq, d), "bf16", with_values)
     tot = sum(lengths)
-    k = _normal(rng, (tot, hkv, d), "bf16")
-    v = _normal(rng, (tot, hkv, d), "bf16")
+    k = _normal(rng, (tot, hkv, d), "bf16", with_values)
+    v = _normal(rng, (tot, hkv, d), "bf16", with_values)
     script, logical = _sequential_script(lengths)
     return Workload(f"block_size_sweep_bs{block_size}", seed, hq, hkv, d, block_size, "bf16",
                     1.0 / math.sqrt(d), nb, free_order, q, k, v, script,
                     list(range(batch)), logical)
 
 
-def prefix_sharing(seed=5, batch=128, prefix_len=2056, max_suffix=512):
+def prefix_sharing(seed=5, batch=128, prefix_len=2056, max_suffix=512, with_values=True):
     """128 sequences forked from one prefix, each with its own suffix.
 
     Sequence 0 is filled with the prefix and forked 127 times, so every
@@ -234,10 +237,10 @@ def prefix_sharing(seed=5, batch=128, prefix_len=2056, max_suffix=512):
     held = prefix_len // bs + sum(-(-(prefix_len + g) // bs) - (prefix_len // bs) for g in grow)
     nb = -(-(11 * held) // 10)
     free_order = rng.permutation(nb).astype(np.int32)
-    q = _normal(rng, (batch, hq, d), "bf16")
+    q = _normal(rng, (batch, hq, d), "bf16", with_values)
     tot = prefix_len + sum(grow)
-    k = _normal(rng, (tot, hkv, d), "bf16")
-    v = _normal(rng, (tot, hkv, d), "bf16")
+    k = _normal(rng, (tot, hkv, d), "bf16", with_values)
+    v = _normal(rng, (tot, hkv, d), "bf16", with_values)
     prefix_rows = np.arange(prefix_len, dtype=np.int64)
     script = [("create", 0), ("reserve", [0], [prefix_len], prefix_rows)]
     script += [("fork", 0, c) for c in range(1, batch)]
