@@ -56,7 +56,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kTile = 16;           // tokens per MFMA tile
 constexpr int kTableChunk = 64;     // table entries held in one VGPR
-constexpr float kLog2e = 1.4426950408889634f;
 
 // --------------------------------------------------------------- utilities
 template <int N>
@@ -73,6 +72,11 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<Begin + 1, End>(f);
   }
 }
+
+// Reinterprets one 32-bit word.  Taking the word by value matters: a
+// __builtin_bit_cast applied directly to an ext_vector element (v[e]) is
+// lowered by this compiler as a cast of element 0 whatever e is.
+__device__ __forceinline__ float as_float(uint32_t w) { return __builtin_bit_cast(float, w); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) {
@@ -337,7 +341,7 @@ __device__ __forceinline__ void consume_tile(SplitState<BF16, D, GP>& st,
     for (int p = 0; p < Geo::kKPieces; ++p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        s = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, r.k[p][e]),
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(as_float(r.k[p][e]),
                                                  qf32[4 * p + e], s, 0, 0, 0);
     }
   }
@@ -370,7 +374,7 @@ __device__ __forceinline__ void consume_tile(SplitState<BF16, D, GP>& st,
         vf[q][2 * w] = ok ? bf16_lo(r.v[q][w]) : 0.f;
         vf[q][2 * w + 1] = ok ? bf16_hi(r.v[q][w]) : 0.f;
       } else {
-        vf[q][w] = ok ? __builtin_bit_cast(float, r.v[q][w]) : 0.f;
+        vf[q][w] = ok ? as_float(r.v[q][w]) : 0.f;
       }
     }
   }
@@ -430,7 +434,7 @@ decode_split_kernel(DecodeArgs a) {
           qf[p] = x;
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) qf32[4 * p + e] = __builtin_bit_cast(float, x[e]);
+          for (int e = 0; e < 4; ++e) qf32[4 * p + e] = as_float(x[e]);
         }
       }
     }
