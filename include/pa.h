@@ -134,8 +134,15 @@ pa_status pa_copy_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, void* 
  * block_size:   must equal desc->block_size.
  * out:          device [num_seqs][num_q_heads][head_dim], pool dtype.
  * workspace:    device scratch of at least pa_decode_workspace_size() bytes,
- *               256-byte aligned; the call owns it until the stream reaches
- *               the end of the call. */
+ *               256-byte aligned, needing no initialisation.  The call owns
+ *               it until the stream reaches the end of the call; calls that
+ *               share a workspace must be ordered (one stream, or events).
+ * num_seqs:     at most 8192 (PA_ERR_UNSUPPORTED beyond, or when the lengths
+ *               snapshot and merge buffers would not fit in LDS).
+ * The work is split over the grid in equal shares of (sequence, KV head,
+ * 16-token tile) units.  A sequence cut by a share boundary leaves partial
+ * results in the workspace, merged by a second small kernel launched on the
+ * same stream by the same call. */
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, int32_t block_size,

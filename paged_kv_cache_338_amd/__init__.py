@@ -201,7 +201,8 @@ def pa_decode_workspace_size(desc, num_seqs, num_q_heads, max_blocks_per_seq):
 
 
 def decode_workspace(k_cache, num_seqs, num_q_heads, max_blocks_per_seq):
-    """Allocates (with torch) a workspace sized for pa_decode."""
+    """Allocates (with torch) a workspace sized for pa_decode.  It needs no
+    initialisation, and one workspace serves any number of ordered calls."""
     torch = _torch()
     n = pa_decode_workspace_size(cache_desc(k_cache), num_seqs, num_q_heads, max_blocks_per_seq)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=k_cache.device)

@@ -1,0 +1,110 @@
+// Slot-mapped append and copy-on-write block copy (gfx950).
+//
+// Sources: "What is paged attention in vLLM, and why does it matter?"
+// (interview.clozo.ai), Step 4: at every decode step the new token's keys
+// and values are written into the sequence's last block; "Paged Attention"
+// (klaylearn.com glossary), body: prefill fills freshly allocated blocks the
+// same way; "PagedAttention - AI Glossary" (modelrefs.com), How it works,
+// item 5, and the clozo.ai Trade-offs section: a block shared by several
+// sequences is copied only when one of them writes into it, and only that
+// block is copied.
+//
+// Both kernels are pure data movement: 16-byte loads and stores, one
+// workgroup per token (append) or per (pair, pool) (copy).  Out-of-pool slots
+// and block ids are skipped, so a bad index never turns into a wild write.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace {
+
+__global__ void __launch_bounds__(256)
+cache_append_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                    const int64_t* __restrict__ slots, uint4* __restrict__ k_cache,
+                    uint4* __restrict__ v_cache, int64_t num_slots, int32_t bs, int32_t heads,
+                    int32_t row_vecs) {
+  const int64_t t = blockIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / bs;
+  const int32_t off = static_cast<int32_t>(slot - blk * bs);
+  const int32_t per = heads * row_vecs;
+  for (int32_t i = threadIdx.x; i < 2 * per; i += blockDim.x) {
+    const bool is_v = i >= per;
+    const int32_t j = is_v ? i - per : i;
+    const int32_t h = j / row_vecs, c = j - h * row_vecs;
+    const uint4 x = (is_v ? v : k)[t * per + j];
+    (is_v ? v_cache : k_cache)[((blk * heads + h) * bs + off) * row_vecs + c] = x;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(const int32_t* __restrict__ pairs, uint4* __restrict__ k_cache,
+                   uint4* __restrict__ v_cache, int32_t num_blocks, int64_t block_vecs) {
+  const int32_t src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint4* base = blockIdx.y ? v_cache : k_cache;
+  const uint4* s = base + src * block_vecs;
+  uint4* d = base + dst * block_vecs;
+  constexpr int kUnroll = 4;
+  int64_t i = threadIdx.x;
+  for (; i + (kUnroll - 1) * 256 < block_vecs; i += kUnroll * 256) {
+    uint4 x[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) x[u] = s[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) d[i + u * 256] = x[u];
+  }
+  for (; i < block_vecs; i += 256) d[i] = s[i];
+}
+
+pa_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pa::fail(PA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_cache_append(const void* k, const void* v, const int64_t* slot_mapping,
+                          int32_t num_tokens, void* k_cache, void* v_cache,
+                          const pa_cache_desc* desc, void* stream) {
+  pa_status st = pa::check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_tokens %d < 0", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  const int32_t row_vecs = desc->head_dim * pa::elem_bytes(desc->dtype) / 16;
+  hipLaunchKernelGGL(cache_append_kernel, dim3(num_tokens), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4*)k, (const uint4*)v, slot_mapping, (uint4*)k_cache,
+                     (uint4*)v_cache, (int64_t)desc->num_blocks * desc->block_size,
+                     desc->block_size, desc->num_kv_heads, row_vecs);
+  return check_launch("pa_cache_append");
+}
+
+pa_status pa_copy_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, void* k_cache,
+                         void* v_cache, const pa_cache_desc* desc, void* stream) {
+  pa_status st = pa::check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_pairs %d < 0", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst_pairs || !k_cache || !v_cache)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (num_pairs > desc->num_blocks)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_pairs %d > num_blocks %d", num_pairs,
+                    desc->num_blocks);
+  const int64_t block_vecs = (int64_t)desc->num_kv_heads * desc->block_size * desc->head_dim *
+                             pa::elem_bytes(desc->dtype) / 16;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, (hipStream_t)stream,
+                     src_dst_pairs, (uint4*)k_cache, (uint4*)v_cache, desc->num_blocks,
+                     block_vecs);
+  return check_launch("pa_copy_blocks");
+}
+
+}  // extern "C"

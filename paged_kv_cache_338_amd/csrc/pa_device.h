@@ -1,0 +1,70 @@
+// Device helpers shared by the library's HIP translation units (gfx950,
+// wave64).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+#include <utility>
+
+namespace pa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// DPP row_newbcast: every lane of a 16-lane row reads lane N of that row.
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
+}
+
+template <int Begin, int End, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (Begin < End) {
+    f(std::integral_constant<int, Begin>{});
+    static_for<Begin + 1, End>(f);
+  }
+}
+
+// Reinterprets one 32-bit word.  Taking the word by value matters: a
+// __builtin_bit_cast applied directly to an ext_vector element (v[e]) is
+// lowered by this compiler as a cast of element 0 whatever e is.
+__device__ __forceinline__ float as_float(uint32_t w) { return __builtin_bit_cast(float, w); }
+
+// bf16 halves of a packed word, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Workgroup barrier that orders LDS only: global loads still in flight are
+// not drained (unlike __syncthreads(), a full workgroup fence).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+}  // namespace pa

@@ -9,4 +9,13 @@ namespace pa {
 // returns `status`, so callers can write `return fail(PA_ERR_..., "...")`.
 pa_status fail(pa_status status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
+// log2 of x if x is a power of two >= 1, else -1.
+int ilog2_exact(int32_t x);
+
+// Bytes per stored value of a pool dtype.
+inline int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
+
+// Validates a pool descriptor against the supported set (see pa.h).
+pa_status check_desc(const pa_cache_desc* desc);
+
 }  // namespace pa
