@@ -29,6 +29,9 @@
  *   outside the pool are skipped (append, copy) or clamped into it (decode,
  *   whose output for such a sequence is then unspecified), and lengths are
  *   clamped to max_blocks_per_seq * block_size.
+ * - Alignment: q, out, k, v, k_cache and v_cache 16 bytes; int64 arrays 8
+ *   bytes; int32 arrays 4 bytes; the decode workspace 256 bytes.  A
+ *   misaligned pointer is PA_ERR_INVALID_ARGUMENT.
  * - KV pool layout: two pools, k_cache and v_cache, each
  *   [num_blocks][num_kv_heads][block_size][head_dim], row-major, values of
  *   the pool's dtype.  One (block, KV head) tile is contiguous.

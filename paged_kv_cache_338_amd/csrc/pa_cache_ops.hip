@@ -80,6 +80,9 @@ pa_status pa_cache_append(const void* k, const void* v, const int64_t* slot_mapp
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !slot_mapping || !k_cache || !v_cache)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!pa::aligned(k, 16) || !pa::aligned(v, 16) || !pa::aligned(k_cache, 16) ||
+      !pa::aligned(v_cache, 16) || !pa::aligned(slot_mapping, 8))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "misaligned pointer");
   const int32_t row_vecs = desc->head_dim * pa::elem_bytes(desc->dtype) / 16;
   hipLaunchKernelGGL(cache_append_kernel, dim3(num_tokens), dim3(256), 0, (hipStream_t)stream,
                      (const uint4*)k, (const uint4*)v, slot_mapping, (uint4*)k_cache,
@@ -96,6 +99,8 @@ pa_status pa_copy_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, void* 
   if (num_pairs == 0) return PA_OK;
   if (!src_dst_pairs || !k_cache || !v_cache)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!pa::aligned(k_cache, 16) || !pa::aligned(v_cache, 16) || !pa::aligned(src_dst_pairs, 4))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "misaligned pointer");
   if (num_pairs > desc->num_blocks)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_pairs %d > num_blocks %d", num_pairs,
                     desc->num_blocks);

@@ -12,31 +12,33 @@
 // Work decomposition:
 //  * A segment is one (sequence b, KV head) pair; it has ceil(L_b / 16)
 //    tiles of 16 tokens.  All tiles of all segments are numbered in one flat
-//    order (b, KV head, tile).  Workgroup w takes the equal share
-//    [T*w/W, T*(w+1)/W) of the T tiles and wave v of the workgroup the
-//    equal contiguous part v of that share, so every wave streams the same
-//    number of K/V bytes whatever the length mix.
-//  * Context lengths are first copied into LDS with their prefix sums over
-//    sequences, so all waves of a workgroup see one consistent snapshot.
-//  * A wave walks its part as pieces, one per segment it meets; each piece
-//    is a straight pipelined loop over its tiles (NBUF tiles of loads in
-//    flight), with the segment's query rows and physical block ids fetched
-//    before the loop.  A segment wholly inside the wave's part is written
-//    out by the wave.  Other pieces leave their online-softmax state in LDS;
-//    after one barrier the leading wave of each such segment merges the
-//    states: into the output if the segment lies inside the workgroup's
-//    share, else into a partial in the workspace.
-//  * A second, small kernel merges the partials of segments cut by share
-//    boundaries (the workgroup that holds a segment's first part leaves a
-//    record for it), so no cross-workgroup synchronisation is needed.
-//  * Per tile: the K rows of the 16 tokens are the A operand of one MFMA
-//    chain (v_mfma_f32_16x16x32_bf16, or 16x16x4_f32 for fp32 pools) whose
-//    B operand is the KV head's G query rows, loaded straight from memory
-//    with 16-byte loads (lane l holds a 16-byte piece of token l % 16's
-//    row).  The logits land in lane 16*j + g (head g, tokens 4j..4j+3); each
-//    16-lane row keeps its own running max and sum.  P*V runs on the VALU in
-//    fp32: lane 16*j + c owns D/16 output columns for the V rows of tokens
-//    4j..4j+3, with the probabilities broadcast by DPP.
+//    order (b, KV head, tile).  Wave w of the W waves of the grid takes the
+//    equal share [T*w/W, T*(w+1)/W) of the T tiles, so every wave streams
+//    the same number of K/V bytes whatever the length mix, and no wave ever
+//    waits for another.
+//  * Each workgroup first copies the context lengths into LDS with their
+//    prefix sums over sequences, so its waves see one consistent snapshot.
+//  * A wave walks its share as pieces, one per segment it meets; each piece
+//    is a branch-free loop over batches of NBUF tiles (all loads of a batch
+//    issued before its first use), with the segment's query rows and
+//    physical block ids fetched ahead.  A segment wholly inside the share
+//    is written out by the wave; a piece of a segment cut by a share
+//    boundary leaves its online-softmax state (max, sum, unnormalised
+//    output) as a partial in the workspace.
+//  * A second, small kernel merges the partials of each cut segment (the
+//    wave that holds its first piece leaves a record for it), so there is
+//    no cross-wave synchronisation inside the decode kernel.
+//  * Per tile (bf16 pools): the K rows of the 16 tokens are the A operand of
+//    a v_mfma_f32_16x16x32_bf16 chain whose B operand is the KV head's G
+//    query rows, so the logits of head g and token 4j+r land in lane 16j+g,
+//    register r.  The probabilities, rounded to bf16, are the A operand of
+//    a v_mfma_f32_16x16x16_bf16 chain against the V rows (D/16 output
+//    column blocks), so the output accumulates in MFMA registers too.
+//    fp32 pools use v_mfma_f32_16x16x4_f32 for the logits and the VALU for
+//    P*V, with the probabilities broadcast by DPP.
+//  * The running max is raised lazily: only when a logit exceeds it by more
+//    than 8 (log2 units) are the sum and output rescaled, so most tiles skip
+//    the rescale.  Any reference value gives the same softmax.
 //  * Blocks of >= 16 tokens are read through a buffer resource spanning the
 //    tile; the padding tiles of the pipeline get a zero-length resource, so
 //    every loop iteration issues the same loads and each use waits only for
@@ -61,13 +63,15 @@ using pa::kWave;
 using pa::u32x4_t;
 
 constexpr int kTile = 16;         // tokens per tile (one MFMA row block)
-constexpr int kMaxWGs = 1024;     // the workspace holds partials for this many workgroups
-constexpr int kDefaultWGs = 256;  // one workgroup per compute unit
+constexpr int kMaxWaves = 4096;   // the workspace holds partials for this many waves
+constexpr int kDefaultWGs = 256;  // workgroups of the decode grid
 constexpr int kMaxSeqs = 8192;    // lengths snapshot in LDS
 constexpr int kRecInts = 8;       // ints per cut-segment record
-constexpr int kTaskHead = 4;      // ints before the contributor slots of a merge task
 constexpr int kMergeWG = 256;     // threads of the partial-merge kernel
 constexpr size_t kMaxLds = 160 * 1024;
+#ifndef PA_DECODE_OCC
+#define PA_DECODE_OCC 2  // waves per SIMD the register budget must allow
+#endif
 #ifndef PA_DECODE_NB_BF16
 #define PA_DECODE_NB_BF16 3  // tiles per batch for bf16 pools (build-time tuning knob)
 #endif
@@ -79,10 +83,10 @@ struct DecodeArgs {
   const int32_t* tables;
   const int32_t* lens;
   void* out;
-  float* ws_o;       // [2 * kMaxWGs][G][D] unnormalised partial outputs
-  float* ws_m;       // [2 * kMaxWGs][G] running max (log2 units)
-  float* ws_l;       // [2 * kMaxWGs][G] sum of exp2(x - max)
-  int32_t* records;  // [kMaxWGs][kRecInts] cut segment led by each workgroup
+  float* ws_o;       // [2 * kMaxWaves][G][D] unnormalised partial outputs
+  float* ws_m;       // [2 * kMaxWaves][G] running max (log2 units)
+  float* ws_l;       // [2 * kMaxWaves][G] sum of exp2(x - max)
+  int32_t* records;  // [kMaxWaves][kRecInts] cut segment whose first piece each wave holds
   int32_t B;
   int32_t max_blocks;
   int32_t num_blocks;
@@ -427,18 +431,17 @@ __device__ __forceinline__ void consume_tile_mfma(MfmaState<D>& st,
   }
   if (__ballot(hi) != 0) {  // uniform: raise the reference
     float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = pa::rows_max(mt);
     const float nref = fmaxf(st.ref, mt);
     const float f = __builtin_amdgcn_exp2f(st.ref - nref);
     st.l *= f;
     st.ref = nref;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float fr = __shfl(f, 4 * jr + q);  // head 4j + q
+    pa::static_for<0, 4>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      const float fr = pa::pick_row_quad<q>(f, jr);  // head 4j + q
 #pragma unroll
       for (int b = 0; b < kBlk; ++b) st.acc[b][q] *= fr;
-    }
+    });
   }
   const f32x2_t p01 = {__builtin_amdgcn_exp2f(x[0] - st.ref), __builtin_amdgcn_exp2f(x[1] - st.ref)};
   const f32x2_t p23 = {__builtin_amdgcn_exp2f(x[2] - st.ref), __builtin_amdgcn_exp2f(x[3] - st.ref)};
@@ -486,42 +489,6 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int32_t b, int32_t k
   }
 }
 
-// Adds n >= 1 softmax partials (max m_i, sum l_i, unnormalised o_i of one
-// output element) by the rescaled-sum rule; `get(i, m, o, l)` fetches
-// partial i.  Partials are fetched kBatch at a time with indices clamped to
-// n - 1 (the extra copies get weight zero), so each batch's loads are issued
-// together, one round trip per batch.
-struct Merged {
-  float mx, acc, den;  // max, unnormalised output, sum; the result is acc / den
-};
-
-template <int kBatch, typename Get>
-__device__ __forceinline__ Merged merge_partials(int32_t n, Get&& get) {
-  float mx = -3.0e38f, acc = 0.f, den = 0.f;
-  for (int32_t i0 = 0; i0 < n; i0 += kBatch) {
-    float pm[kBatch], po[kBatch], pl[kBatch];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) get(min(i0 + k, n - 1), pm[k], po[k], pl[k]);
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k)
-      if (i0 + k >= n) pm[k] = -3.0e38f;
-    float cm = mx;
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) cm = fmaxf(cm, pm[k]);
-    const float r = __builtin_amdgcn_exp2f(mx - cm);
-    acc *= r;
-    den *= r;
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const float f = i0 + k < n ? __builtin_amdgcn_exp2f(pm[k] - cm) : 0.f;
-      acc = fmaf(f, po[k], acc);
-      den = fmaf(f, pl[k], den);
-    }
-    mx = cm;
-  }
-  return Merged{mx, acc, den};
-}
-
 // Largest w with floor(T * w / W) <= f: the share (of W equal shares of T
 // units) that holds unit f, for 0 <= f < T.
 __device__ __forceinline__ int32_t share_of(int32_t f, int32_t T, int32_t W) {
@@ -536,23 +503,20 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x) {
 
 template <bool BF16, int D, int GP, int kNW, int NBUF, bool kSmall>
 __global__ void __launch_bounds__(kNW * kWave)
+__attribute__((amdgpu_waves_per_eu((kSmall && (BF16 || GP * D < 16 * 128)) ? PA_DECODE_OCC : 1)))
 decode_kernel(DecodeArgs a) {
   using Geo = Geometry<BF16, D>;
   constexpr int kWG = kNW * kWave;
-  constexpr int kTaskInts = kTaskHead + kNW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), v = tid >> 6;
   const int jr = lane >> 4, c16 = lane & 15;
   const int32_t wg = blockIdx.x, nwg = gridDim.x;
   const int32_t B = a.B, H_kv = a.H_kv, G = a.G, H_q = H_kv * G;
 
-  // LDS: per wave two parked states (o[G][D], m[G], l[G]), then the lengths.
-  const int32_t slot_floats = G * D + 2 * G;
-  float* lds_st = reinterpret_cast<float*>(smem);                       // [kNW][2][slot]
-  int32_t* PB = reinterpret_cast<int32_t*>(lds_st + kNW * 2 * slot_floats);  // [B + 1]
-  int32_t* Ls = PB + B + 1;                                            // [B]
-  int32_t* misc = Ls + B;                                              // [kNW]
-  int32_t* tasks = misc + kNW;                                         // [2 * kNW][kTaskInts]
+  // LDS: the lengths snapshot and its prefix sums.
+  int32_t* PB = reinterpret_cast<int32_t*>(smem);  // [B + 1]
+  int32_t* Ls = PB + B + 1;                        // [B]
+  int32_t* misc = Ls + B;                          // [kNW]
 
   // ---- lengths snapshot and prefix sums of tiles per sequence
   const int32_t len_cap = a.max_blocks << a.log2_bs;
@@ -584,9 +548,6 @@ decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int32_t Tt = uni(PB[B]) * H_kv;  // flat tiles (host bounds it below 2^31)
-  const int32_t F0 = static_cast<int32_t>((int64_t)Tt * wg / nwg);
-  const int32_t F1 = static_cast<int32_t>((int64_t)Tt * (wg + 1) / nwg);
-  int32_t* rec = a.records + wg * kRecInts;
 
   // Sequences with no context get a zero row (workgroup b % W writes it).
   for (int32_t b = wg; b < B; b += nwg) {
@@ -595,67 +556,249 @@ decode_kernel(DecodeArgs a) {
         store_out<BF16>(a.out, (int64_t)b * H_q * D + e, 0.f);
     }
   }
-  if (F0 >= F1) {
-    if (tid == 0) rec[0] = 0;
-    return;
-  }
-
-  // ---- this wave's contiguous part [G0, G1) of the share
-  const int32_t span = F1 - F0;
-  auto part_start = [&](int32_t w) { return F0 + static_cast<int32_t>((int64_t)span * w / kNW); };
-  const int32_t G0 = part_start(v), G1 = part_start(v + 1);
+  // ---- this wave's share [G0, G1): wave wv of Wt, the equal share
+  // [T*wv/Wt, T*(wv+1)/Wt) of the flat tiles.
+  const int32_t Wt = nwg * kNW, wv = wg * kNW + v;
+  const int32_t G0 = static_cast<int32_t>((int64_t)Tt * wv / Wt);
+  const int32_t G1 = static_cast<int32_t>((int64_t)Tt * (wv + 1) / Wt);
   const int log2_bs = a.log2_bs;
   const int nbt = log2_bs >= 4 ? 1 : (kTile >> log2_bs);  // table lanes per tile
   const int tpc_log = log2_bs >= 4 ? 6 : 2 + log2_bs;       // log2(tiles per table chunk)
-  auto slot_ptr = [&](int w, int k) { return lds_st + (w * 2 + k) * slot_floats; };
+  int32_t* rec = a.records + wv * kRecInts;
+  bool first_of_cut = false;  // this wave holds the first piece of a cut segment
+  Seg cut{};
+
+  using State = std::conditional_t<BF16, MfmaState<D>, WaveState<false, D, GP>>;
+  // Finishes segment s after its last tile in this share.  A segment wholly
+  // inside the share is written out; a cut piece leaves (max, sum,
+  // unnormalised output) in partial slot 2*wv + 0 if the segment began
+  // before the share, else 2*wv + 1.
+  auto finish = [&](const State& st, const Seg s) {
+    const bool whole = s.S0 >= G0 && s.S1 <= G1;
+    const int32_t pslot = 2 * wv + (s.S0 < G0 ? 0 : 1);
+    float* slot = a.ws_o + (int64_t)pslot * G * D;
+    if (!whole && s.S0 >= G0) {
+      first_of_cut = true;
+      cut = s;
+    }
+    if constexpr (BF16) {
+      // ---- finish the piece: sums over the 4 rows; the accumulators
+      // already hold whole tiles (lane 16j + c, register r: head 4j + r).
+      constexpr int kBlk = D / 16;
+      float lt = st.l;
+      lt = pa::rows_sum(lt);
+      pa::static_for<0, 4>([&](auto Q) {
+        constexpr int q = decltype(Q)::value;
+        const int g = 4 * jr + q;
+        const float lg = pa::pick_row_quad<q>(lt, jr);  // head g's sum
+        if (g < G) {
+          if (whole) {
+            const float inv = 1.f / lg;
+            uint32_t pk[kBlk / 2];
+#pragma unroll
+            for (int i = 0; i < kBlk / 2; ++i) {
+              const f32x2_t pr = {st.acc[2 * i][q] * inv, st.acc[2 * i + 1][q] * inv};
+              pk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+            }
+            char* dst = reinterpret_cast<char*>(a.out) +
+                        ((((int64_t)s.b * H_kv + s.kvh) * G + g) * D + kBlk * c16) * 2;
+            if constexpr (kBlk == 8) *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+            else *reinterpret_cast<uint2*>(dst) = uint2{pk[0], pk[1]};
+          } else {
+            float* dst = slot + g * D + kBlk * c16;
+#pragma unroll
+            for (int i = 0; i < kBlk; ++i) dst[i] = st.acc[i][q];
+          }
+        }
+      });
+      if (!whole && lane < G) {
+        a.ws_m[pslot * G + lane] = st.ref;
+        a.ws_l[pslot * G + lane] = lt;
+      }
+    } else {
+      // ---- merge the 4 row states (lanes g, 16+g, 32+g, 48+g hold head g)
+      const float M = pa::rows_max(st.m);
+      const float sc = exp2f(st.m - M);
+      const float lt = pa::rows_sum(st.l * sc);
+      pa::static_for<0, GP>([&](auto gi) {
+        constexpr int g = decltype(gi)::value;
+        const float f = pa::row_bcast<g>(sc);
+        const float inv = 1.f / pa::row_bcast<g>(lt);
+        float o[Geo::kCols];
+#pragma unroll
+        for (int c = 0; c < Geo::kCols; ++c) {
+          o[c] = pa::rows_sum(st.o[g][c] * f);
+        }
+        if (g < G && (g & 3) == jr) {
+          if (whole) {
+            const int64_t base = (((int64_t)s.b * H_kv + s.kvh) * G + g) * D + c16 * Geo::kCols;
+#pragma unroll
+            for (int c = 0; c < Geo::kCols; ++c) store_out<BF16>(a.out, base + c, o[c] * inv);
+          } else {
+#pragma unroll
+            for (int c = 0; c < Geo::kCols; ++c) slot[g * D + c16 * Geo::kCols + c] = o[c];
+          }
+        }
+      });
+      if (!whole && lane < G) {
+        a.ws_m[pslot * G + lane] = M;
+        a.ws_l[pslot * G + lane] = lt;
+      }
+    }
+  };
 
   if (G0 < G1) {
-    Seg s = seg_containing(PB, Ls, B, H_kv, G0);
-    while (true) {
-      // ---- one piece: tiles [t0, t0 + n) of segment s
-      const int32_t t0 = max(s.S0, G0) - s.S0;
-      const int32_t n = min(s.S1, G1) - s.S0 - t0;
-      u32x4_t qf[Geo::kQRegs];
-      float qf32[Geo::kQF32];
-      load_q<BF16, D>(a, s.b, s.kvh, qf, qf32, lane);
-      // The loop body has no branches: padding steps past the piece's
-      // last tile issue zero-length loads and consume a fully masked tile
-      // (a no-op on the state), so every use waits only for its own loads.
-      std::conditional_t<BF16, MfmaState<D>, WaveState<false, D, GP>> st;
-      st.reset();
-      TileRegs<BF16, D> buf[NBUF];
-      auto consume = [&](const TileRegs<BF16, D>& r, int32_t j) {
-        const int32_t tok0 = kTile * (t0 + j);
-        const int32_t end = j < n ? s.L : tok0;  // padding: every row masked
-        if constexpr (BF16) consume_tile_mfma<D>(st, r, qf, a.scale_log2, tok0, end, G, lane);
-        else consume_tile(st, r, qf, qf32, a.scale_log2, tok0, end, lane);
+    State st;
+    st.reset();
+    if constexpr (!kSmall) {
+      // ---- the share as a stream of batches of up to NBUF tiles.  A batch
+      // holds the remaining tiles of one segment A and, if A ends inside
+      // it, the first tiles of the next segment B, so a share that crosses
+      // a segment boundary costs no extra round trip.  The block ids of the
+      // next batch are fetched (scalar loads; the table is read-only during
+      // the kernel) while the current batch is consumed, and the query rows
+      // of A and B are loaded with the batch's tiles.
+      struct Batch {
+        Seg A, B;
+        int32_t fa;      // flat index of the batch's first tile (in A)
+        int32_t nA, n;   // tiles of A; tiles in all (the rest are B's)
+        bool endA, endB; // the segment's last tile in this share is here
       };
-      if constexpr (!kSmall) {
-        // Physical block ids by scalar loads (the table is read-only during
-        // the kernel), one tile ahead of their use.
-        const int32_t __attribute__((address_space(4)))* trow =
-            (const int32_t __attribute__((address_space(4)))*)uniform_ptr(
-                reinterpret_cast<const char*>(a.tables + (int64_t)s.b * a.max_blocks));
-        auto phys_of = [&](int32_t j) -> int32_t {
-          return trow[uni(((t0 + min(j, n - 1)) * kTile) >> log2_bs)];
-        };
-        // Batches: each iteration issues the loads of NBUF tiles, then
-        // consumes them, so no load is in flight across the loop's back edge
-        // (the other waves of the SIMD cover the gap between batches).
-        for (int32_t j0 = 0; j0 < n; j0 += NBUF) {
-          int32_t ph[NBUF];
-#pragma unroll
-          for (int u = 0; u < NBUF; ++u) ph[u] = phys_of(j0 + u);
-#pragma unroll
-          for (int u = 0; u < NBUF; ++u)
-            issue_tile<BF16, D>(buf[u], a, ph[u], t0 + min(j0 + u, n - 1), s.kvh, lane,
-                                j0 + u < n);
-          // Keep every load of the batch ahead of the first use: left alone,
-          // the scheduler sinks loads next to their uses to save registers.
-          __builtin_amdgcn_sched_barrier(0);
-          pa::static_for<0, NBUF>([&](auto U) { consume(buf[decltype(U)::value], j0 + decltype(U)::value); });
+      Seg cs = seg_containing(PB, Ls, B, H_kv, G0);
+      int32_t f = G0;  // next flat tile of the share
+      auto next = [&]() {
+        Batch bt;
+        bt.A = cs;
+        bt.B = cs;
+        bt.fa = f;
+        // An exhausted cursor (S0 past f) yields an empty batch.
+        const int32_t limA = min(cs.S1, G1);
+        bt.nA = cs.S0 <= f ? max(min(NBUF, limA - f), 0) : 0;
+        bt.endA = bt.nA > 0 && f + bt.nA == limA;
+        f += bt.nA;
+        bt.n = bt.nA;
+        if (bt.nA > 0 && f == cs.S1 && f < G1) {
+          seg_advance(cs, PB, Ls, B, H_kv);
+          if (bt.nA < NBUF && cs.S0 == f) {
+            bt.B = cs;
+            const int32_t limB = min(cs.S1, G1);
+            const int32_t nB = min(NBUF - bt.nA, limB - f);
+            bt.endB = f + nB == limB;
+            f += nB;
+            bt.n += nB;
+            if (f == cs.S1 && f < G1) seg_advance(cs, PB, Ls, B, H_kv);
+          }
         }
-      } else {
+        if (bt.n == bt.nA) bt.endB = false;
+        return bt;
+      };
+      // Segment and in-segment tile of batch slot u.
+      auto slot_tile = [&](const Batch& bt, int u, int32_t& kvh, int32_t& t) {
+        const int32_t uu = min(u, max(bt.n - 1, 0));
+        const bool inA = uu < bt.nA;
+        kvh = inA ? bt.A.kvh : bt.B.kvh;
+        t = bt.fa + uu - (inA ? bt.A.S0 : bt.B.S0);
+      };
+      // Block ids of the share, 64 tiles at a time: lane i of chunk c holds
+      // the physical block of flat tile G0 + 64c + i (clamped to the share),
+      // found by a per-lane search of the lengths snapshot and one vector
+      // load from the table, so batches read their block ids from registers
+      // and the table is never on a batch's critical path.
+      auto chunk_phys = [&](int32_t c) -> int32_t {
+        const int32_t fl = min(G0 + 64 * c + lane, G1 - 1);
+        const int32_t b = find_seq(PB, B, H_kv, fl);
+        const int32_t pb = PB[b];
+        const int32_t nt = max(PB[b + 1] - pb, 1);
+        const int32_t r = fl - pb * H_kv;
+        const int32_t t = r - (r / nt) * nt;
+        return a.tables[(int64_t)b * a.max_blocks + ((t * kTile) >> log2_bs)];
+      };
+      int32_t cbase = G0;  // flat tile of lane 0 of chunk `cur`
+      int32_t cur = chunk_phys(0), nxt = chunk_phys(1);
+      // Block ids of a batch's tiles, read from the chunks into SGPRs.
+      // They are taken for batch k+1 before batch k is consumed, when the
+      // chunks are known to have arrived, so that the loop head waits for
+      // nothing before issuing the next batch.
+      auto batch_phys = [&](const Batch& bt, int32_t (&ph)[NBUF]) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          const int32_t i = uni(min(bt.fa + min(u, max(bt.n - 1, 0)) - cbase, 127));
+          ph[u] = i < 64 ? __builtin_amdgcn_readlane(cur, i) : __builtin_amdgcn_readlane(nxt, i - 64);
+        }
+      };
+      Batch bt = next();
+      int32_t ph[NBUF];
+      batch_phys(bt, ph);
+      while (true) {
+        u32x4_t qa[Geo::kQRegs], qb[Geo::kQRegs];
+        float qa32[Geo::kQF32], qb32[Geo::kQF32];
+        load_q<BF16, D>(a, bt.A.b, bt.A.kvh, qa, qa32, lane);
+        load_q<BF16, D>(a, bt.B.b, bt.B.kvh, qb, qb32, lane);
+        TileRegs<BF16, D> buf[NBUF];
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          int32_t kvh, t;
+          slot_tile(bt, u, kvh, t);
+          issue_tile<BF16, D>(buf[u], a, ph[u], t, kvh, lane, u < bt.n);
+        }
+        const Batch nx = next();
+        batch_phys(nx, ph);
+        if (nx.n > 0 && nx.fa + nx.n - 1 + NBUF - cbase >= 128) {
+          // The batch after nx may leave the window [cbase, cbase + 128):
+          // slide it by one chunk now, a batch ahead, so that a chunk is
+          // never read in the iteration that loads it (batches are shorter
+          // than a chunk, so that batch lies inside the new window).
+          cbase += 64;
+          cur = nxt;
+          nxt = chunk_phys((cbase - G0) / 64 + 1);
+        }
+        // Keep every load of the batch ahead of the first use: left alone,
+        // the scheduler sinks loads next to their uses to save registers.
+        __builtin_amdgcn_sched_barrier(0);
+        pa::static_for<0, NBUF>([&](auto U) {
+          constexpr int u = decltype(U)::value;
+          if (u < bt.nA) {
+            const int32_t tok0 = kTile * (bt.fa + u - bt.A.S0);
+            if constexpr (BF16) consume_tile_mfma<D>(st, buf[u], qa, a.scale_log2, tok0, bt.A.L, G, lane);
+            else consume_tile(st, buf[u], qa, qa32, a.scale_log2, tok0, bt.A.L, lane);
+          }
+        });
+        if (bt.endA) {
+          finish(st, bt.A);
+          st.reset();
+        }
+        pa::static_for<0, NBUF>([&](auto U) {
+          constexpr int u = decltype(U)::value;
+          if (u >= bt.nA && u < bt.n) {
+            const int32_t tok0 = kTile * (bt.fa + u - bt.B.S0);
+            if constexpr (BF16) consume_tile_mfma<D>(st, buf[u], qb, a.scale_log2, tok0, bt.B.L, G, lane);
+            else consume_tile(st, buf[u], qb, qb32, a.scale_log2, tok0, bt.B.L, lane);
+          }
+        });
+        if (bt.endB) {
+          finish(st, bt.B);
+          st.reset();
+        }
+        if (nx.n == 0) break;
+        bt = nx;
+      }
+    } else {
+      // ---- blocks smaller than a tile: the share as pieces, one per
+      // segment, each a pipelined loop over its tiles.
+      Seg s = seg_containing(PB, Ls, B, H_kv, G0);
+      while (true) {
+        const int32_t t0 = max(s.S0, G0) - s.S0;
+        const int32_t n = min(s.S1, G1) - s.S0 - t0;
+        u32x4_t qf[Geo::kQRegs];
+        float qf32[Geo::kQF32];
+        load_q<BF16, D>(a, s.b, s.kvh, qf, qf32, lane);
+        TileRegs<BF16, D> buf[NBUF];
+        auto consume = [&](const TileRegs<BF16, D>& r, int32_t j) {
+          const int32_t tok0 = kTile * (t0 + j);
+          const int32_t end = j < n ? s.L : tok0;  // padding: every row masked
+          if constexpr (BF16) consume_tile_mfma<D>(st, r, qf, a.scale_log2, tok0, end, G, lane);
+          else consume_tile(st, r, qf, qf32, a.scale_log2, tok0, end, lane);
+        };
         // Blocks smaller than a tile: block ids of a chunk of tiles in a
         // VGPR (one per lane), one chunk ahead.  Lanes past the piece repeat
         // its last tile, so the gather is unconditional.
@@ -687,199 +830,122 @@ decode_kernel(DecodeArgs a) {
             consume(buf[u], j);
           });
         }
-      }
-
-      const bool whole = s.S0 >= G0 && s.S1 <= G1;
-      float* slot = slot_ptr(v, s.S0 < G0 ? 0 : 1);
-      if constexpr (BF16) {
-        // ---- finish the piece: sums over the 4 rows; the accumulators
-        // already hold whole tiles (lane 16j + c, register r: head 4j + r).
-        constexpr int kBlk = D / 16;
-        float lt = st.l;
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int g = 4 * jr + q;
-          const float lg = __shfl(lt, g);  // lane g holds head g's sum
-          if (g < G) {
-            if (whole) {
-              const float inv = 1.f / lg;
-              uint32_t wv[kBlk / 2];
-#pragma unroll
-              for (int i = 0; i < kBlk / 2; ++i) {
-                const f32x2_t pr = {st.acc[2 * i][q] * inv, st.acc[2 * i + 1][q] * inv};
-                wv[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
-              }
-              char* dst = reinterpret_cast<char*>(a.out) +
-                          ((((int64_t)s.b * H_kv + s.kvh) * G + g) * D + kBlk * c16) * 2;
-              if constexpr (kBlk == 8) *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
-              else *reinterpret_cast<uint2*>(dst) = uint2{wv[0], wv[1]};
-            } else {
-              float* dst = slot + g * D + kBlk * c16;
-#pragma unroll
-              for (int i = 0; i < kBlk; ++i) dst[i] = st.acc[i][q];
-            }
-          }
-        }
-        if (!whole && lane < G) {
-          slot[G * D + lane] = st.ref;
-          slot[G * D + G + lane] = lt;
-        }
-      } else {
-      // ---- merge the 4 row states (lanes g, 16+g, 32+g, 48+g hold head g)
-        float M = fmaxf(st.m, __shfl_xor(st.m, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
-        const float sc = exp2f(st.m - M);
-        float lt = st.l * sc;
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
-        pa::static_for<0, GP>([&](auto gi) {
-          constexpr int g = decltype(gi)::value;
-          const float f = pa::row_bcast<g>(sc);
-          const float inv = 1.f / pa::row_bcast<g>(lt);
-          float o[Geo::kCols];
-#pragma unroll
-          for (int c = 0; c < Geo::kCols; ++c) {
-            o[c] = st.o[g][c] * f;
-            o[c] += __shfl_xor(o[c], 16);
-            o[c] += __shfl_xor(o[c], 32);
-          }
-          if (g < G && (g & 3) == jr) {
-            if (whole) {
-              const int64_t base = (((int64_t)s.b * H_kv + s.kvh) * G + g) * D + c16 * Geo::kCols;
-#pragma unroll
-              for (int c = 0; c < Geo::kCols; ++c) store_out<BF16>(a.out, base + c, o[c] * inv);
-            } else {
-#pragma unroll
-              for (int c = 0; c < Geo::kCols; ++c) slot[g * D + c16 * Geo::kCols + c] = o[c];
-            }
-          }
-        });
-        if (!whole && lane < G) {
-          slot[G * D + lane] = M;
-          slot[G * D + G + lane] = lt;
-        }
-      }
-      if (s.S1 >= G1) break;
-      seg_advance(s, PB, Ls, B, H_kv);
-    }
-  }
-  __syncthreads();
-
-  // ---- merge the parked states.  The first wave with tiles leads the
-  // segment the share starts inside; every wave leads the segment it ends
-  // inside if that segment starts within the wave's part.  The contributors
-  // of a segment are the waves whose parts meet it (with fewer tiles than
-  // waves, each non-empty part is one tile); wave w keeps its piece in slot 0
-  // if the segment began before its part, else in slot 1.  Leaders post
-  // their tasks to LDS; then every thread of the workgroup merges.
-  const int32_t first_wave = share_of(0, span, kNW);  // the wave whose part holds tile F0
-  for (int k = 0; k < 2; ++k) {
-    int32_t* task = tasks + (v * 2 + k) * kTaskInts;
-    bool lead = false;
-    Seg s{};
-    if (G0 < G1) {
-      s = seg_containing(PB, Ls, B, H_kv, k == 0 ? G0 : G1 - 1);
-      lead = k == 0 ? (v == first_wave && s.S0 < F0) : (s.S1 > G1 && s.S0 >= G0);
-    }
-    if (lane == 0) task[0] = lead ? 1 : 0;
-    if (!lead) continue;
-    const int32_t lo = max(s.S0, F0), hi = min(s.S1, F1);
-    const int32_t va = share_of(lo - F0, span, kNW);
-    const int32_t nc = span >= kNW ? share_of(hi - 1 - F0, span, kNW) - va + 1 : hi - lo;
-    if (lane < nc) {
-      const int32_t w = span >= kNW ? va + lane : share_of(lo + lane - F0, span, kNW);
-      task[kTaskHead + lane] = (w * 2 + (s.S0 < part_start(w) ? 0 : 1)) * slot_floats;
-    }
-    if (lane == 0) {
-      task[1] = nc;
-      task[2] = (s.b * H_kv + s.kvh) * G;                       // output row of head 0
-      task[3] = (s.S0 >= F0 && s.S1 <= F1) ? -1 : 2 * wg + (s.S0 < F0 ? 0 : 1);  // partial slot
-    }
-  }
-  pa::lds_barrier();
-  for (int t = 0; t < 2 * kNW; ++t) {
-    const int32_t* task = tasks + t * kTaskInts;
-    if (task[0] == 0) continue;  // uniform
-    const int32_t nc = task[1], orow = task[2], wslot = task[3];
-    for (int32_t e = tid; e < G * D; e += kWG) {
-      const int32_t g = e / D;
-      const Merged x = merge_partials<kNW>(nc, [&](int32_t i, float& m, float& o, float& l) {
-        const float* st = lds_st + task[kTaskHead + i];
-        m = st[G * D + g];
-        o = st[e];
-        l = st[G * D + G + g];
-      });
-      if (wslot < 0) {
-        store_out<BF16>(a.out, (int64_t)orow * D + e, x.acc / x.den);
-      } else {
-        // Partial for the merge kernel: (max, sum, unnormalised output).
-        a.ws_o[(int64_t)wslot * G * D + e] = x.acc;
-        if (e - g * D == 0) {
-          a.ws_m[wslot * G + g] = x.mx;
-          a.ws_l[wslot * G + g] = x.den;
-        }
+        finish(st, s);
+        if (s.S1 >= G1) break;
+        st.reset();
+        seg_advance(s, PB, Ls, B, H_kv);
       }
     }
   }
-
-  // ---- record for the partial-merge kernel: the segment this share ends
-  // inside, if it also starts inside the share (this workgroup holds its
-  // first part).
-  if (tid == 0) {
-    const Seg s = seg_containing(PB, Ls, B, H_kv, F1 - 1);
-    const bool first = s.S1 > F1 && s.S0 >= F0;
-    rec[0] = first ? 1 : 0;
-    rec[1] = s.b;
-    rec[2] = s.kvh;
-    rec[3] = s.S0;
-    rec[4] = s.S1;
+  // ---- record for the partial-merge kernel: the cut segment whose first
+  // piece this wave holds (at most one: its last piece).
+  if (lane == 0) {
+    rec[0] = first_of_cut ? 1 : 0;
+    rec[1] = cut.b;
+    rec[2] = cut.kvh;
+    rec[3] = cut.S0;
+    rec[4] = cut.S1;
     rec[5] = Tt;
   }
 }
 
-// Merges the partials of the segment recorded by workgroup blockIdx.x of
-// the decode kernel (grid of W workgroups).  The contributors are the
-// shares that meet the segment: consecutive shares from the recording one
-// when every share is non-empty (T >= W), else one share per tile.  The
-// first contributor's partial is in slot 2w + 1, every later one in slot 2w.
+// Merges the partials of the segment recorded by wave blockIdx.x of the
+// decode kernel (W waves in all), for query head blockIdx.y of the group.
+// The contributors are the waves whose shares meet the segment:
+// consecutive ones from the recording wave when every share is non-empty
+// (T >= W), else one share per tile.  The first contributor's partial is in
+// slot 2w + 1, every later one in slot 2w.  Thread t takes the 4-column
+// group t % (D/4) of the head's row for the contributors congruent to
+// t / (D/4); the slices' (max, sum, output) are then combined through LDS,
+// so the dependent-load depth is n / (number of slices), not n.
 template <bool BF16, int D>
 __global__ void __launch_bounds__(kMergeWG)
 merge_kernel(DecodeArgs a) {
-  __shared__ int32_t slots[kMaxWGs];
+  constexpr int kCols = D / 4;
+  constexpr int kSlices = kMergeWG / kCols;
+  constexpr int kBatch = 4;  // contributors per thread in flight
+  __shared__ floatx4_t s_acc[kSlices][kCols];
+  __shared__ float s_mx[kSlices], s_den[kSlices];
   const int32_t* rec = a.records + blockIdx.x * kRecInts;
   if (rec[0] == 0) return;
-  const int32_t W = gridDim.x, G = a.G;
+  const int32_t W = gridDim.x, G = a.G, g = blockIdx.y;
   const int32_t b = rec[1], kvh = rec[2], S0 = rec[3], S1 = rec[4], Tt = rec[5];
   const int32_t wa = blockIdx.x;
-  // With one tile per non-empty share (T < W <= kMaxWGs), the share of tile
-  // f is ((f + 1) W - 1) / T, small enough for 32-bit arithmetic.
+  // With one tile per non-empty share (T < W <= kMaxWaves), the share of
+  // tile f is ((f + 1) W - 1) / T, small enough for 32-bit arithmetic.
   const int32_t n = Tt >= W ? share_of(S1 - 1, Tt, W) - wa + 1 : S1 - S0;
-  for (int32_t i = threadIdx.x; i < n; i += kMergeWG) {
+  auto slot_of = [&](int32_t i) {
     const int32_t w = Tt >= W ? wa + i : ((S0 + i + 1) * W - 1) / Tt;
-    slots[i] = 2 * w + (i == 0 ? 1 : 0);
+    return 2 * w + (i == 0 ? 1 : 0);
+  };
+  const int col = threadIdx.x % kCols, k = threadIdx.x / kCols;
+  float mx = -3.0e38f, den = 0.f;
+  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int32_t i0 = k; i0 < n; i0 += kSlices * kBatch) {
+    // Unconditional loads (indices past n repeat contributor i0), masked
+    // afterwards, so every load of the batch is in flight at once.
+    float pm[kBatch], pl[kBatch];
+    floatx4_t po[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int32_t i = i0 + u * kSlices;
+      const int32_t slot = slot_of(i < n ? i : i0);
+      pm[u] = a.ws_m[slot * G + g];
+      pl[u] = a.ws_l[slot * G + g];
+      po[u] = *reinterpret_cast<const floatx4_t*>(a.ws_o + ((int64_t)slot * G + g) * D + 4 * col);
+    }
+    float cm = mx;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (i0 + u * kSlices < n) cm = fmaxf(cm, pm[u]);
+    const float r = __builtin_amdgcn_exp2f(mx - cm);
+    acc *= r;
+    den *= r;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float f = i0 + u * kSlices < n ? __builtin_amdgcn_exp2f(pm[u] - cm) : 0.f;
+      acc += f * po[u];
+      den = fmaf(f, pl[u], den);
+    }
+    mx = cm;
+  }
+  s_acc[k][col] = acc;
+  if (col == 0) {
+    s_mx[k] = mx;
+    s_den[k] = den;
   }
   __syncthreads();
-  for (int32_t e = threadIdx.x; e < G * D; e += kMergeWG) {
-    const int32_t g = e / D;
-    const Merged x = merge_partials<8>(n, [&](int32_t i, float& m, float& o, float& l) {
-      const int32_t slot = slots[i];
-      m = a.ws_m[slot * G + g];
-      o = a.ws_o[(int64_t)slot * G * D + e];
-      l = a.ws_l[slot * G + g];
-    });
-    store_out<BF16>(a.out, ((int64_t)b * a.H_kv + kvh) * G * D + e, x.acc / x.den);
+  if (k != 0) return;
+  float M = s_mx[0];
+#pragma unroll
+  for (int j = 1; j < kSlices; ++j) M = fmaxf(M, s_mx[j]);
+  floatx4_t o = {0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+#pragma unroll
+  for (int j = 0; j < kSlices; ++j) {
+    const float f = __builtin_amdgcn_exp2f(s_mx[j] - M);  // 0 for an empty slice
+    o += f * s_acc[j][col];
+    l = fmaf(f, s_den[j], l);
+  }
+  const float inv = 1.f / l;
+  const int64_t base = (((int64_t)b * a.H_kv + kvh) * G + g) * D + 4 * col;
+  if constexpr (BF16) {
+    const f32x2_t lo = {o[0] * inv, o[1] * inv}, hi = {o[2] * inv, o[3] * inv};
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + base) =
+        uint2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
+              __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t))};
+  } else {
+    *reinterpret_cast<floatx4_t*>(reinterpret_cast<float*>(a.out) + base) = o * inv;
   }
 }
 
 // ----------------------------------------------------------- host helpers
-int decode_wgs() {
+int decode_wgs(int nw) {
   // Tuning override (read on every call): PA_DECODE_WGS = workgroups of
   // the decode grid.  Any value gives the same result up to fp32 rounding.
   const char* e = std::getenv("PA_DECODE_WGS");
   const int x = e ? std::atoi(e) : kDefaultWGs;
-  return x >= 1 && x <= kMaxWGs ? x : kDefaultWGs;
+  return x >= 1 && x * nw <= kMaxWaves ? x : kDefaultWGs;
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -892,33 +958,32 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t H_q) {
   const size_t G = H_q / d->num_kv_heads;
   WorkspaceLayout w;
   w.rec_off = 0;
-  w.o_off = align_up((size_t)kMaxWGs * kRecInts * sizeof(int32_t), 256);
-  w.m_off = w.o_off + align_up((size_t)2 * kMaxWGs * G * d->head_dim * sizeof(float), 256);
-  w.l_off = w.m_off + align_up((size_t)2 * kMaxWGs * G * sizeof(float), 256);
-  w.total = w.l_off + align_up((size_t)2 * kMaxWGs * G * sizeof(float), 256);
+  w.o_off = align_up((size_t)kMaxWaves * kRecInts * sizeof(int32_t), 256);
+  w.m_off = w.o_off + align_up((size_t)2 * kMaxWaves * G * d->head_dim * sizeof(float), 256);
+  w.l_off = w.m_off + align_up((size_t)2 * kMaxWaves * G * sizeof(float), 256);
+  w.total = w.l_off + align_up((size_t)2 * kMaxWaves * G * sizeof(float), 256);
   return w;
 }
 
-// Waves per workgroup and tiles in flight per wave, chosen so that the
-// live registers stay under the budget of two waves per SIMD (one for the
-// largest query groups).
-template <bool BF16, int GP>
+// Waves per workgroup and tiles per batch.  Waves are independent, so the
+// workgroup size only sets how often the lengths prologue is repeated.
+template <bool BF16, int D, int GP>
 struct Config {
-  static constexpr int kNW = GP >= 16 ? 4 : 8;
-  static constexpr int NBUF = GP >= 8 ? 2 : (BF16 ? PA_DECODE_NB_BF16 : 2);
+  static constexpr int kNW = 4;
+  // fp32 pools with large query groups hold G*D/16 output floats per lane
+  // in registers, which leaves room for one tile per batch only.
+  static constexpr int NBUF =
+      BF16 ? (GP >= 8 ? 2 : PA_DECODE_NB_BF16) : (GP * D >= 8 * 64 ? 1 : 2);
 };
 
-size_t lds_bytes(int nw, int32_t G, int32_t D, int32_t B) {
-  return (size_t)nw * 2 * (G * D + 2 * G) * sizeof(float) +
-         (size_t)(2 * B + 1 + nw + 2 * nw * (kTaskHead + nw)) * sizeof(int32_t);
-}
+size_t lds_bytes(int nw, int32_t B) { return (size_t)(2 * B + 1 + nw) * sizeof(int32_t); }
 
 template <bool BF16, int D, int GP>
 pa_status launch(const DecodeArgs& a, hipStream_t s) {
-  using C = Config<BF16, GP>;
+  using C = Config<BF16, D, GP>;
   auto kern = a.log2_bs >= 4 ? decode_kernel<BF16, D, GP, C::kNW, C::NBUF, false>
                              : decode_kernel<BF16, D, GP, C::kNW, C::NBUF, true>;
-  const size_t lds = lds_bytes(C::kNW, a.G, D, a.B);
+  const size_t lds = lds_bytes(C::kNW, a.B);
   if (lds > kMaxLds)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: %d sequences need %zu bytes of LDS (> %zu)",
                     a.B, lds, kMaxLds);
@@ -928,10 +993,9 @@ pa_status launch(const DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess)
       return pa::fail(PA_ERR_DEVICE, "pa_decode: LDS attribute: %s", hipGetErrorString(e));
   }
-  const int wgs = decode_wgs();
+  const int wgs = decode_wgs(C::kNW);
   hipLaunchKernelGGL(kern, dim3(wgs), dim3(C::kNW * kWave), lds, s, a);
-  if (wgs > 1)
-    hipLaunchKernelGGL((merge_kernel<BF16, D>), dim3(wgs), dim3(kMergeWG), 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<BF16, D>), dim3(wgs * C::kNW, a.G), dim3(kMergeWG), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_DEVICE, "pa_decode: %s", hipGetErrorString(e));
   return PA_OK;
@@ -1001,8 +1065,11 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");
-  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+  if (!pa::aligned(workspace, 256))
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if (!pa::aligned(q, 16) || !pa::aligned(k_cache, 16) || !pa::aligned(v_cache, 16) ||
+      !pa::aligned(out, 16) || !pa::aligned(block_tables, 4) || !pa::aligned(context_lens, 4))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "misaligned pointer");
   const WorkspaceLayout wl = workspace_layout(desc, num_q_heads);
   if (workspace_bytes < wl.total)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace %zu bytes < %zu needed", workspace_bytes,

@@ -58,6 +58,40 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48) with
+// the gfx950 row-swap permutes: no LDS traffic, so they do not share the
+// LGKM counter with scalar loads in flight.  permlane32_swap of x with
+// itself leaves {x[l], x[l^32]} in its two results on every lane, and
+// permlane16_swap leaves {x[l], x[l^16]}.
+__device__ __forceinline__ float rows_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = as_float(a[0]) + as_float(a[1]);
+  const uint32_t w = __builtin_bit_cast(uint32_t, y);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return as_float(b[0]) + as_float(b[1]);
+}
+__device__ __forceinline__ float rows_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = fmaxf(as_float(a[0]), as_float(a[1]));
+  const uint32_t w = __builtin_bit_cast(uint32_t, y);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(as_float(b[0]), as_float(b[1]));
+}
+
+// Lane 16j + c receives x from lane 4j + Q (row j picks its own source;
+// the sources lie in lanes 0..15).  Read through SGPRs, without LDS.
+template <int Q>
+__device__ __forceinline__ float pick_row_quad(float x, int jr) {
+  const int xi = __builtin_bit_cast(int, x);
+  const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, Q));
+  const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 4 + Q));
+  const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 8 + Q));
+  const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 12 + Q));
+  return jr == 0 ? s0 : (jr == 1 ? s1 : (jr == 2 ? s2 : s3));
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {

@@ -18,4 +18,9 @@ inline int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
 // Validates a pool descriptor against the supported set (see pa.h).
 pa_status check_desc(const pa_cache_desc* desc);
 
+// True if p is a multiple of `bytes` (a power of two).
+inline bool aligned(const void* p, uintptr_t bytes) {
+  return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
+}
+
 }  // namespace pa

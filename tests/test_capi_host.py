@@ -72,6 +72,17 @@ def test_device_entry_points_validate_on_the_host():
         pa.PA_ERR_INVALID_ARGUMENT
     assert lib.pa_copy_blocks(None, 17, ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.byref(d),
                               None) == pa.PA_ERR_INVALID_ARGUMENT
+    # Misaligned device pointers (never dereferenced: rejected on the host).
+    p16, p8 = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)
+    assert lib.pa_copy_blocks(ctypes.c_void_p(1 << 20), 1, p16, p8, ctypes.byref(d), None) == \
+        pa.PA_ERR_INVALID_ARGUMENT and b"misaligned" in lib.pa_last_error()
+    assert lib.pa_cache_append(p16, p8, ctypes.c_void_p(1 << 20), 1, p16, p16, ctypes.byref(d),
+                               None) == pa.PA_ERR_INVALID_ARGUMENT
+    assert b"misaligned" in lib.pa_last_error()
+    ws = ctypes.c_void_p(1 << 24)
+    st_ = lib.pa_decode(p16, p16, p16, p16, 4, p16, 2, 16, 1.0, p8, 32, ctypes.byref(d), ws,
+                        n.value, None)
+    assert st_ == pa.PA_ERR_INVALID_ARGUMENT and b"misaligned" in lib.pa_last_error()
 
 
 # ------------------------------------------------------------- allocator
