@@ -12,14 +12,17 @@ One timed step is one decode step of the whole model's attention path:
   * for each of the 32 layers (each with its own K/V pool, so the step reads
     1.4 GB and cannot be served from the 256 MB last-level cache):
     pa_copy_blocks (only if the allocator reported pairs), pa_cache_append of
-    the new token's K/V, pa_decode.
+    the new token's K/V, pa_decode.  The layer loop enqueues only kernel
+    launches, so it is captured once as a HIP graph and replayed every step
+    (--eager launches each call from Python instead).
 Lengths grow by one token per step, as in real decoding; the KV bytes of
 every step are counted exactly.
 
 Reported: value = KV bytes read by pa_decode per second over the timed steps
 (GB/s, whole step, all host work included).  roofline: pa_decode alone,
-timed with HIP events around back-to-back launches over the 32 layer pools
-at the batch's exact lengths, against the 8 TB/s HBM peak.  cpu_baseline:
+timed with HIP events around back-to-back launches (a replayed graph of the
+32 layers' calls) at the batch's exact lengths, against the 8 TB/s HBM
+peak; one launch is the whole call, its two kernels included.  cpu_baseline:
 the CPU oracle's paged decode on the same batch (one layer), timed on this
 host.
 """
@@ -57,6 +60,8 @@ def parse():
                    help="passes over the layer pools for the pa_decode roofline timing")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", action="store_true",
+                   help="launch every call from Python instead of replaying a captured HIP graph")
     return p.parse_args()
 
 
@@ -160,18 +165,39 @@ def main():
     torch.cuda.synchronize()
     log("prefill done")
 
-    # ---- roofline leg: pa_decode alone, back-to-back over the layer pools
+    # ---- roofline leg: pa_decode alone, back-to-back over the layer pools.
+    # The calls only enqueue kernels (no allocation, no memset), so they are
+    # captured once in a HIP graph and replayed: the timing is then the
+    # GPU's, not Python's launch rate.
     stream = torch.cuda.current_stream()
-    dec = [pa.prepare_decode(q, kpool[l], vpool[l], tables_d, lens_d, bs, w.scale, outs[l], ws)
-           for l in range(nl)]
-    for l in range(nl):
-        dec[l]()
+
+    def captured(make_calls):
+        """Calls made on the capture stream, and a replay function."""
+        if args.eager:
+            calls = make_calls()
+            return lambda: [c() for c in calls]
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            calls = make_calls()  # prepared on the capture stream
+            for c in calls:  # eager run first: library loaded, attributes set
+                c()
+            side.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                for c in calls:
+                    c()
+        torch.cuda.synchronize()
+        return g.replay
+
+    run_dec = captured(lambda: [pa.prepare_decode(q, kpool[l], vpool[l], tables_d, lens_d, bs,
+                                                  w.scale, outs[l], ws) for l in range(nl)])
+    run_dec()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.kernel_reps):
-        for l in range(nl):
-            dec[l]()
+        run_dec()
     e1.record(stream)
     torch.cuda.synchronize()
     launches = args.kernel_reps * nl
@@ -190,7 +216,15 @@ def main():
                 ev=torch.cuda.Event()) for _ in range(2)]
     slots_d = torch.empty(B, dtype=torch.int64, device=dev)
     pairs_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
-    app = [pa.prepare_cache_append(new_k, new_v, slots_d, kpool[l], vpool[l]) for l in range(nl)]
+
+    def layer_calls():
+        calls = []
+        for l in range(nl):
+            calls.append(pa.prepare_cache_append(new_k, new_v, slots_d, kpool[l], vpool[l]))
+            calls.append(pa.prepare_decode(q, kpool[l], vpool[l], tables_d, lens_d, bs, w.scale,
+                                           outs[l], ws))
+        return calls
+
     seq_ids = np.array(w.seq_ids, np.int64)
     ones = np.ones(B, np.int32)
     kv_read = []
@@ -212,12 +246,15 @@ def main():
             pairs_d[:npairs].copy_(buf["pairs"][:npairs], non_blocking=True)
         buf["ev"].record(stream)
         kv_read.append(int(buf["lens"].numpy().sum()) * kv_bytes_per_token(w) * nl)
-        for l in range(nl):
-            if npairs:
+        if npairs:  # copy-on-write before the step's appends (none in this batch)
+            for l in range(nl):
                 pa.prepare_copy_blocks(pairs_d, npairs, kpool[l], vpool[l])()
-            app[l]()
-            dec[l]()
+        run_layers()
 
+    # The device uploads of the first step happen before capture so that the
+    # captured appends write real slots (replays write the step's own).
+    slots_d.fill_(-1)  # capture-time eager run: every append slot skipped
+    run_layers = captured(layer_calls)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -235,14 +272,16 @@ def main():
     value = sum(kv_read) / (ms_step * args.steps * 1e-3) / 1e9
     log(f"steps: {ms_step:.3f} ms/step ({ms_step * 1e3 / nl:.2f} us/layer), {value:.0f} GB/s")
 
+    mode = "eager launches" if args.eager else "HIP graph replay of the layer loop"
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "llama3_8b_decode: per step, host slot reservation + table upload, "
-                               f"then {nl} layers x (pa_cache_append + pa_decode); 32 Q / 8 KV "
-                               "heads, head 128, bs 16, bf16, pool 4096 blocks per layer",
+                               f"then {nl} layers x (pa_cache_append + pa_decode) by {mode}; "
+                               "32 Q / 8 KV heads, head 128, bs 16, bf16, pool 4096 blocks "
+                               "per layer",
                    "batch": B, "context_lens_at_first_step": (L0 + args.warmup + 1).tolist(),
                    "tokens_added_per_step": B, "layers": nl,
                    "us_per_layer": round(ms_step * 1e3 / nl, 3)},

@@ -292,3 +292,59 @@ def test_workspace_needs_no_initialisation_and_is_reusable(monkeypatch):
         pa.pa_decode(qd, gc.k_cache, gc.v_cache, td, ld, w.block_size, w.scale, out, workspace=ws)
         torch.cuda.synchronize()
         assert_close(w, out, want)
+
+
+def test_graph_replay_matches_eager_and_reads_lengths_at_run_time():
+    # pa_cache_append and pa_decode enqueue only kernel launches (no memset,
+    # no allocation), so a captured HIP graph replays them; the decode reads
+    # the lengths from device memory at run time, so a replay after the
+    # lengths change follows them.  Each replay is checked, with eager work
+    # and synchronisations in between.
+    import torch
+    import paged_kv_cache_338_amd as pa
+    w = W.llama3_8b_decode()
+    oc, gc = run_both(w)
+    tables, lens = gc.tables()
+    qd = _gd().to_torch(w.q, w.dtype, gc.device)
+    td = torch.from_numpy(tables).to(gc.device)
+    ld = torch.from_numpy(lens).to(gc.device)
+    # Re-append the last token of every sequence (same rows, same slots).
+    last = np.array([len(r) - 1 for r in w.logical_rows])
+    rows = np.array([w.logical_rows[b][last[b]] for b in range(w.batch)])
+    slots = np.array([tables[b, last[b] // w.block_size] * w.block_size + last[b] % w.block_size
+                      for b in range(w.batch)], np.int64)
+    kr = gc.k_rows.index_select(0, torch.from_numpy(rows).to(gc.device)).contiguous()
+    vr = gc.v_rows.index_select(0, torch.from_numpy(rows).to(gc.device)).contiguous()
+    sd = torch.from_numpy(slots).to(gc.device)
+    ws = pa.decode_workspace(gc.k_cache, w.batch, w.num_q_heads, tables.shape[1])
+    out_e = torch.empty_like(qd)
+    pa.pa_decode(qd, gc.k_cache, gc.v_cache, td, ld, w.block_size, w.scale, out_e, workspace=ws)
+    torch.cuda.synchronize()
+    want = oc.decode()
+    assert_close(w, out_e, want)
+
+    out_g = torch.empty_like(qd)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pa.pa_cache_append(kr, vr, sd, gc.k_cache, gc.v_cache)
+            pa.pa_decode(qd, gc.k_cache, gc.v_cache, td, ld, w.block_size, w.scale, out_g,
+                         workspace=ws)
+    torch.cuda.synchronize()
+    short = np.maximum(lens - 37, 1).astype(np.int32)
+    want_short = oc.decode(tables=tables, lens=short)
+    for rep in range(4):
+        use_short = rep == 2
+        ld.copy_(torch.from_numpy(short if use_short else lens))
+        out_g.fill_(float("nan"))
+        # eager work on the same workspace and stream between replays
+        tmp = torch.empty_like(qd)
+        pa.pa_decode(qd, gc.k_cache, gc.v_cache, td, ld, w.block_size, w.scale, tmp, workspace=ws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g.view(torch.int16), tmp.view(torch.int16)), rep
+        assert_close(w, out_g, want_short if use_short else want)
+    assert_pools_equal(w, gc, oc)
