@@ -69,6 +69,12 @@ constexpr int kMaxSeqs = 8192;    // lengths snapshot in LDS
 constexpr int kRecInts = 8;       // ints per cut-segment record
 constexpr int kMergeWG = 256;     // threads of the partial-merge kernel
 constexpr size_t kMaxLds = 160 * 1024;
+#ifndef PA_DECODE_NW
+#define PA_DECODE_NW 4  // waves per workgroup
+#endif
+#ifndef PA_DECODE_OCC_STREAM
+#define PA_DECODE_OCC_STREAM 1  // waves per SIMD the streamed path's registers must allow
+#endif
 #ifndef PA_DECODE_OCC
 #define PA_DECODE_OCC 2  // waves per SIMD the register budget must allow
 #endif
@@ -86,7 +92,7 @@ struct DecodeArgs {
   float* ws_o;       // [2 * kMaxWaves][G][D] unnormalised partial outputs
   float* ws_m;       // [2 * kMaxWaves][G] running max (log2 units)
   float* ws_l;       // [2 * kMaxWaves][G] sum of exp2(x - max)
-  int32_t* records;  // [kMaxWaves][kRecInts] cut segment whose first piece each wave holds
+  int32_t* records;  // [B * H_kv][kRecInts] per segment: cut? and its contributors
   int32_t B;
   int32_t max_blocks;
   int32_t num_blocks;
@@ -158,8 +164,8 @@ __device__ __forceinline__ Seg seg_containing(const int32_t* PB, const int32_t* 
   Seg s;
   s.b = uni(find_seq(PB, B, H_kv, f));
   const int32_t pb = uni(PB[s.b]);
-  s.nt = uni(PB[s.b + 1]) - pb;
-  s.kvh = (f - pb * H_kv) / s.nt;
+  s.nt = max(uni(PB[s.b + 1]) - pb, 1);
+  s.kvh = min((f - pb * H_kv) / s.nt, H_kv - 1);
   s.S0 = pb * H_kv + s.kvh * s.nt;
   s.S1 = s.S0 + s.nt;
   s.L = uni(Ls[s.b]);
@@ -379,20 +385,20 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Per-wave state over one piece, bf16 pools (P*V by MFMA).
 //  ref: lane 16j + g: reference max of head g (log2 units), equal in all rows.
-//  l:   lane 16j + g: sum of the (bf16-rounded) weights of head g over the
-//       tokens of row j.
+//  l:   lane 16j + c, register r: sum of the (bf16-rounded) weights of head
+//       4j + r, equal in every column c (an MFMA of P against ones).
 //  acc[blk]: lane 16j + c, register r: unnormalised output of head 4j + r at
 //       column (D/16)*c + blk.
 template <int D>
 struct MfmaState {
   static constexpr int kBlk = D / 16;
   float ref;
-  float l;
+  floatx4_t l;
   floatx4_t acc[kBlk];
 
   __device__ __forceinline__ void reset() {
     ref = -3.0e38f;
-    l = 0.f;
+    l = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int b = 0; b < kBlk; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -403,30 +409,31 @@ struct MfmaState {
 // max that is raised (and the accumulators rescaled) only when a logit
 // exceeds it by more than 2^8, so the common tile needs no cross-lane
 // reduction; then O += P V by MFMA with P (heads x tokens) exactly where the
-// logits are and V (tokens x columns) made from the lane's own V rows.
-// Weights past the context length (or for heads >= G) are zero, and so are
-// V rows past the context length, so garbage in unused slots cannot leak.
-template <int D>
-__device__ __forceinline__ void consume_tile_mfma(MfmaState<D>& st,
-                                                  const TileRegs<true, D>& r,
-                                                  const u32x4_t* qf, float scale_log2,
-                                                  int32_t t0, int32_t end, int32_t G, int lane) {
+// logits are and V (tokens x columns) made from the lane's own V rows, and
+// l += P 1 by one more MFMA.  Only a tail tile (past the context length)
+// masks: its logits there become -inf (weight 0) and its V rows there
+// become 0, so garbage or NaN in unused slots cannot leak.  Heads >= G have
+// zero query rows; their rows are computed and never stored.
+template <int D, bool kTail>
+__device__ __forceinline__ void consume_tile_mfma_impl(MfmaState<D>& st,
+                                                       const TileRegs<true, D>& r,
+                                                       const u32x4_t* qf, float scale_log2,
+                                                       int32_t t0, int32_t end, int lane) {
   using Geo = Geometry<true, D>;
   constexpr int kBlk = MfmaState<D>::kBlk;
-  const int jr = lane >> 4, c16 = lane & 15;
+  const int jr = lane >> 4;
   floatx4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < Geo::kKPieces; ++p)
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[p]),
                                                 __builtin_bit_cast(bf16x8_t, qf[p]), s, 0, 0, 0);
-  const bool tail = t0 + kTile > end;  // uniform
-  const bool live = c16 < G;
   float x[4];
   bool hi = false;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     x[q] = s[q] * scale_log2;
-    if (!live || t0 + jr * 4 + q >= end) x[q] = -INFINITY;
+    if constexpr (kTail)
+      if (t0 + jr * 4 + q >= end) x[q] = -INFINITY;
     hi = hi || x[q] > st.ref + 8.f;
   }
   if (__ballot(hi) != 0) {  // uniform: raise the reference
@@ -434,11 +441,11 @@ __device__ __forceinline__ void consume_tile_mfma(MfmaState<D>& st,
     mt = pa::rows_max(mt);
     const float nref = fmaxf(st.ref, mt);
     const float f = __builtin_amdgcn_exp2f(st.ref - nref);
-    st.l *= f;
     st.ref = nref;
     pa::static_for<0, 4>([&](auto Q) {
       constexpr int q = decltype(Q)::value;
       const float fr = pa::pick_row_quad<q>(f, jr);  // head 4j + q
+      st.l[q] *= fr;
 #pragma unroll
       for (int b = 0; b < kBlk; ++b) st.acc[b][q] *= fr;
     });
@@ -447,10 +454,9 @@ __device__ __forceinline__ void consume_tile_mfma(MfmaState<D>& st,
   const f32x2_t p23 = {__builtin_amdgcn_exp2f(x[2] - st.ref), __builtin_amdgcn_exp2f(x[3] - st.ref)};
   const uint32_t a01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t));
   const uint32_t a23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t));
-  st.l += (pa::bf16_lo(a01) + pa::bf16_hi(a01)) + (pa::bf16_lo(a23) + pa::bf16_hi(a23));
   const s16x4_t pa_ = __builtin_bit_cast(s16x4_t, (uint64_t)a01 | ((uint64_t)a23 << 32));
   uint32_t m01 = 0xFFFFFFFFu, m23 = 0xFFFFFFFFu;
-  if (tail) {
+  if constexpr (kTail) {
     const int32_t row0 = t0 + jr * 4;
     m01 = (row0 + 0 < end ? 0x0000FFFFu : 0u) | (row0 + 1 < end ? 0xFFFF0000u : 0u);
     m23 = (row0 + 2 < end ? 0x0000FFFFu : 0u) | (row0 + 3 < end ? 0xFFFF0000u : 0u);
@@ -459,11 +465,29 @@ __device__ __forceinline__ void consume_tile_mfma(MfmaState<D>& st,
   for (int b = 0; b < kBlk; ++b) {
     const int w = b >> 1;
     const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
-    const uint32_t v01 = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel) & m01;
-    const uint32_t v23 = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel) & m23;
+    uint32_t v01 = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel);
+    uint32_t v23 = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel);
+    if constexpr (kTail) {
+      v01 &= m01;
+      v23 &= m23;
+    }
     const s16x4_t vb = __builtin_bit_cast(s16x4_t, (uint64_t)v01 | ((uint64_t)v23 << 32));
     st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_, vb, st.acc[b], 0, 0, 0);
   }
+  const s16x4_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
+  st.l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_, ones, st.l, 0, 0, 0);
+}
+
+// kSplit: take the unmasked variant for whole tiles (a uniform branch);
+// otherwise always mask (one code copy, for register-tight callers).
+template <int D, bool kSplit>
+__device__ __forceinline__ void consume_tile_mfma(MfmaState<D>& st, const TileRegs<true, D>& r,
+                                                  const u32x4_t* qf, float scale_log2,
+                                                  int32_t t0, int32_t end, int lane) {
+  if (kSplit && t0 + kTile <= end)
+    consume_tile_mfma_impl<D, false>(st, r, qf, scale_log2, t0, end, lane);
+  else
+    consume_tile_mfma_impl<D, true>(st, r, qf, scale_log2, t0, end, lane);
 }
 
 // Loads the G query rows of segment (b, kvh) as the MFMA B operand (lane
@@ -503,7 +527,8 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x) {
 
 template <bool BF16, int D, int GP, int kNW, int NBUF, bool kSmall>
 __global__ void __launch_bounds__(kNW * kWave)
-__attribute__((amdgpu_waves_per_eu((kSmall && (BF16 || GP * D < 16 * 128)) ? PA_DECODE_OCC : 1)))
+__attribute__((amdgpu_waves_per_eu(kSmall ? ((BF16 || GP * D < 16 * 128) ? PA_DECODE_OCC : 1)
+                                          : PA_DECODE_OCC_STREAM)))
 decode_kernel(DecodeArgs a) {
   using Geo = Geometry<BF16, D>;
   constexpr int kWG = kNW * kWave;
@@ -530,7 +555,7 @@ decode_kernel(DecodeArgs a) {
       Ls[b] = L;
     }
     const int32_t nt = (L + kTile - 1) / kTile;
-    const int32_t incl = pa::wave_incl_scan(nt, lane);
+    const int32_t incl = pa::wave_incl_scan(nt);
     if (lane == kWave - 1) misc[v] = incl;
     __syncthreads();
     int32_t pre = carry, tot = 0;
@@ -554,19 +579,24 @@ decode_kernel(DecodeArgs a) {
     if (Ls[b] == 0) {
       for (int32_t e = tid; e < H_q * D; e += kWG)
         store_out<BF16>(a.out, (int64_t)b * H_q * D + e, 0.f);
+      for (int32_t h = tid; h < H_kv; h += kWG) a.records[(b * H_kv + h) * kRecInts] = 0;
     }
   }
   // ---- this wave's share [G0, G1): wave wv of Wt, the equal share
   // [T*wv/Wt, T*(wv+1)/Wt) of the flat tiles.
   const int32_t Wt = nwg * kNW, wv = wg * kNW + v;
-  const int32_t G0 = static_cast<int32_t>((int64_t)Tt * wv / Wt);
-  const int32_t G1 = static_cast<int32_t>((int64_t)Tt * (wv + 1) / Wt);
+  // floor(Tt * w / Wt) in 32-bit arithmetic: Tt = qt * Wt + rt with rt < Wt
+  // <= 4096, so rt * w < 2^24 (64-bit division would cost hundreds of
+  // instructions on the critical path of every wave).
+  const uint32_t qt = static_cast<uint32_t>(Tt) / static_cast<uint32_t>(Wt);
+  const uint32_t rt = static_cast<uint32_t>(Tt) - qt * static_cast<uint32_t>(Wt);
+  auto bound = [&](uint32_t w) {
+    return static_cast<int32_t>(qt * w + rt * w / static_cast<uint32_t>(Wt));
+  };
+  const int32_t G0 = uni(bound(wv)), G1 = uni(bound(wv + 1));
   const int log2_bs = a.log2_bs;
   const int nbt = log2_bs >= 4 ? 1 : (kTile >> log2_bs);  // table lanes per tile
   const int tpc_log = log2_bs >= 4 ? 6 : 2 + log2_bs;       // log2(tiles per table chunk)
-  int32_t* rec = a.records + wv * kRecInts;
-  bool first_of_cut = false;  // this wave holds the first piece of a cut segment
-  Seg cut{};
 
   using State = std::conditional_t<BF16, MfmaState<D>, WaveState<false, D, GP>>;
   // Finishes segment s after its last tile in this share.  A segment wholly
@@ -577,20 +607,25 @@ decode_kernel(DecodeArgs a) {
     const bool whole = s.S0 >= G0 && s.S1 <= G1;
     const int32_t pslot = 2 * wv + (s.S0 < G0 ? 0 : 1);
     float* slot = a.ws_o + (int64_t)pslot * G * D;
-    if (!whole && s.S0 >= G0) {
-      first_of_cut = true;
-      cut = s;
+    if (s.S0 >= G0 && lane == 0) {
+      // This wave holds the segment's first tile: it writes the segment's
+      // record for the merge kernel (cut or not, tile range, decomposition).
+      int32_t* rec = a.records + (s.b * H_kv + s.kvh) * kRecInts;
+      rec[0] = whole ? 0 : 1;
+      rec[1] = s.S0;
+      rec[2] = s.S1;
+      rec[3] = Tt;
+      rec[4] = Wt;
+      rec[5] = wv;
     }
     if constexpr (BF16) {
       // ---- finish the piece: sums over the 4 rows; the accumulators
       // already hold whole tiles (lane 16j + c, register r: head 4j + r).
       constexpr int kBlk = D / 16;
-      float lt = st.l;
-      lt = pa::rows_sum(lt);
       pa::static_for<0, 4>([&](auto Q) {
         constexpr int q = decltype(Q)::value;
         const int g = 4 * jr + q;
-        const float lg = pa::pick_row_quad<q>(lt, jr);  // head g's sum
+        const float lg = st.l[q];  // head g's sum
         if (g < G) {
           if (whole) {
             const float inv = 1.f / lg;
@@ -610,11 +645,9 @@ decode_kernel(DecodeArgs a) {
             for (int i = 0; i < kBlk; ++i) dst[i] = st.acc[i][q];
           }
         }
+        if (!whole && c16 == 0 && g < G) a.ws_l[pslot * G + g] = lg;
       });
-      if (!whole && lane < G) {
-        a.ws_m[pslot * G + lane] = st.ref;
-        a.ws_l[pslot * G + lane] = lt;
-      }
+      if (!whole && lane < G) a.ws_m[pslot * G + lane] = st.ref;
     } else {
       // ---- merge the 4 row states (lanes g, 16+g, 32+g, 48+g hold head g)
       const float M = pa::rows_max(st.m);
@@ -704,6 +737,8 @@ decode_kernel(DecodeArgs a) {
       // found by a per-lane search of the lengths snapshot and one vector
       // load from the table, so batches read their block ids from registers
       // and the table is never on a batch's critical path.
+      // Indices are clamped into the table so that no snapshot, however
+      // inconsistent, can send a read outside it.
       auto chunk_phys = [&](int32_t c) -> int32_t {
         const int32_t fl = min(G0 + 64 * c + lane, G1 - 1);
         const int32_t b = find_seq(PB, B, H_kv, fl);
@@ -711,10 +746,12 @@ decode_kernel(DecodeArgs a) {
         const int32_t nt = max(PB[b + 1] - pb, 1);
         const int32_t r = fl - pb * H_kv;
         const int32_t t = r - (r / nt) * nt;
-        return a.tables[(int64_t)b * a.max_blocks + ((t * kTile) >> log2_bs)];
+        const int32_t e = min(max((t * kTile) >> log2_bs, 0), a.max_blocks - 1);
+        return a.tables[(int64_t)b * a.max_blocks + e];
       };
       int32_t cbase = G0;  // flat tile of lane 0 of chunk `cur`
-      int32_t cur = chunk_phys(0), nxt = chunk_phys(1);
+      int32_t cur = chunk_phys(0), nxt = 0;
+      if (G1 - G0 > 64) nxt = chunk_phys(1);  // read only by shares of more than 64 tiles
       // Block ids of a batch's tiles, read from the chunks into SGPRs.
       // They are taken for batch k+1 before batch k is consumed, when the
       // chunks are known to have arrived, so that the loop head waits for
@@ -759,7 +796,7 @@ decode_kernel(DecodeArgs a) {
           constexpr int u = decltype(U)::value;
           if (u < bt.nA) {
             const int32_t tok0 = kTile * (bt.fa + u - bt.A.S0);
-            if constexpr (BF16) consume_tile_mfma<D>(st, buf[u], qa, a.scale_log2, tok0, bt.A.L, G, lane);
+            if constexpr (BF16) consume_tile_mfma<D, true>(st, buf[u], qa, a.scale_log2, tok0, bt.A.L, lane);
             else consume_tile(st, buf[u], qa, qa32, a.scale_log2, tok0, bt.A.L, lane);
           }
         });
@@ -771,7 +808,7 @@ decode_kernel(DecodeArgs a) {
           constexpr int u = decltype(U)::value;
           if (u >= bt.nA && u < bt.n) {
             const int32_t tok0 = kTile * (bt.fa + u - bt.B.S0);
-            if constexpr (BF16) consume_tile_mfma<D>(st, buf[u], qb, a.scale_log2, tok0, bt.B.L, G, lane);
+            if constexpr (BF16) consume_tile_mfma<D, true>(st, buf[u], qb, a.scale_log2, tok0, bt.B.L, lane);
             else consume_tile(st, buf[u], qb, qb32, a.scale_log2, tok0, bt.B.L, lane);
           }
         });
@@ -796,7 +833,7 @@ decode_kernel(DecodeArgs a) {
         auto consume = [&](const TileRegs<BF16, D>& r, int32_t j) {
           const int32_t tok0 = kTile * (t0 + j);
           const int32_t end = j < n ? s.L : tok0;  // padding: every row masked
-          if constexpr (BF16) consume_tile_mfma<D>(st, r, qf, a.scale_log2, tok0, end, G, lane);
+          if constexpr (BF16) consume_tile_mfma<D, false>(st, r, qf, a.scale_log2, tok0, end, lane);
           else consume_tile(st, r, qf, qf32, a.scale_log2, tok0, end, lane);
         };
         // Blocks smaller than a tile: block ids of a chunk of tiles in a
@@ -837,40 +874,31 @@ decode_kernel(DecodeArgs a) {
       }
     }
   }
-  // ---- record for the partial-merge kernel: the cut segment whose first
-  // piece this wave holds (at most one: its last piece).
-  if (lane == 0) {
-    rec[0] = first_of_cut ? 1 : 0;
-    rec[1] = cut.b;
-    rec[2] = cut.kvh;
-    rec[3] = cut.S0;
-    rec[4] = cut.S1;
-    rec[5] = Tt;
-  }
 }
 
-// Merges the partials of the segment recorded by wave blockIdx.x of the
-// decode kernel (W waves in all), for query head blockIdx.y of the group.
-// The contributors are the waves whose shares meet the segment:
-// consecutive ones from the recording wave when every share is non-empty
-// (T >= W), else one share per tile.  The first contributor's partial is in
-// slot 2w + 1, every later one in slot 2w.  Thread t takes the 4-column
-// group t % (D/4) of the head's row for the contributors congruent to
-// t / (D/4); the slices' (max, sum, output) are then combined through LDS,
-// so the dependent-load depth is n / (number of slices), not n.
+// Merges the partials of segment blockIdx.x (sequence blockIdx.x / H_kv,
+// KV head blockIdx.x % H_kv) for query head blockIdx.y of the group, if the
+// decode kernel's record says the segment was cut.  The contributors are the
+// waves whose shares meet the segment: consecutive ones from the wave wa
+// holding its first tile when every share is non-empty (T >= W), else one
+// share per tile.  The first contributor's partial is in slot 2w + 1, every
+// later one in slot 2w.  Thread t takes the 4-column group t % (D/4) of the
+// head's row for the contributors congruent to t / (D/4); the slices'
+// (max, sum, output) are then combined through LDS, so the dependent-load
+// depth is n / (number of slices), not n.
 template <bool BF16, int D>
 __global__ void __launch_bounds__(kMergeWG)
 merge_kernel(DecodeArgs a) {
   constexpr int kCols = D / 4;
   constexpr int kSlices = kMergeWG / kCols;
-  constexpr int kBatch = 4;  // contributors per thread in flight
+  constexpr int kBatch = 8;  // contributors per thread in flight
   __shared__ floatx4_t s_acc[kSlices][kCols];
   __shared__ float s_mx[kSlices], s_den[kSlices];
   const int32_t* rec = a.records + blockIdx.x * kRecInts;
   if (rec[0] == 0) return;
-  const int32_t W = gridDim.x, G = a.G, g = blockIdx.y;
-  const int32_t b = rec[1], kvh = rec[2], S0 = rec[3], S1 = rec[4], Tt = rec[5];
-  const int32_t wa = blockIdx.x;
+  const int32_t G = a.G, g = blockIdx.y;
+  const int32_t b = blockIdx.x / a.H_kv, kvh = blockIdx.x % a.H_kv;
+  const int32_t S0 = rec[1], S1 = rec[2], Tt = rec[3], W = rec[4], wa = rec[5];
   // With one tile per non-empty share (T < W <= kMaxWaves), the share of
   // tile f is ((f + 1) W - 1) / T, small enough for 32-bit arithmetic.
   const int32_t n = Tt >= W ? share_of(S1 - 1, Tt, W) - wa + 1 : S1 - S0;
@@ -954,11 +982,11 @@ struct WorkspaceLayout {
   size_t rec_off, o_off, m_off, l_off, total;
 };
 
-WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t H_q) {
+WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t H_q, int32_t B) {
   const size_t G = H_q / d->num_kv_heads;
   WorkspaceLayout w;
   w.rec_off = 0;
-  w.o_off = align_up((size_t)kMaxWaves * kRecInts * sizeof(int32_t), 256);
+  w.o_off = align_up((size_t)B * d->num_kv_heads * kRecInts * sizeof(int32_t), 256);
   w.m_off = w.o_off + align_up((size_t)2 * kMaxWaves * G * d->head_dim * sizeof(float), 256);
   w.l_off = w.m_off + align_up((size_t)2 * kMaxWaves * G * sizeof(float), 256);
   w.total = w.l_off + align_up((size_t)2 * kMaxWaves * G * sizeof(float), 256);
@@ -969,7 +997,7 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t H_q) {
 // workgroup size only sets how often the lengths prologue is repeated.
 template <bool BF16, int D, int GP>
 struct Config {
-  static constexpr int kNW = 4;
+  static constexpr int kNW = PA_DECODE_NW;
   // fp32 pools with large query groups hold G*D/16 output floats per lane
   // in registers, which leaves room for one tile per batch only.
   static constexpr int NBUF =
@@ -995,7 +1023,7 @@ pa_status launch(const DecodeArgs& a, hipStream_t s) {
   }
   const int wgs = decode_wgs(C::kNW);
   hipLaunchKernelGGL(kern, dim3(wgs), dim3(C::kNW * kWave), lds, s, a);
-  hipLaunchKernelGGL((merge_kernel<BF16, D>), dim3(wgs * C::kNW, a.G), dim3(kMergeWG), 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<BF16, D>), dim3(a.B * a.H_kv, a.G), dim3(kMergeWG), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_DEVICE, "pa_decode: %s", hipGetErrorString(e));
   return PA_OK;
@@ -1036,7 +1064,7 @@ pa_status pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
                     max_blocks_per_seq);
   if (num_seqs > kMaxSeqs)
     return pa::fail(PA_ERR_UNSUPPORTED, "num_seqs %d > %d", num_seqs, kMaxSeqs);
-  *bytes = workspace_layout(desc, num_q_heads).total;
+  *bytes = workspace_layout(desc, num_q_heads, num_seqs).total;
   return PA_OK;
 }
 
@@ -1058,7 +1086,10 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   const int64_t len_cap = (int64_t)max_blocks_per_seq * block_size;
   if (len_cap > INT32_MAX)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq * block_size overflows int32");
-  // Flat tile indices (sequence, KV head, tile) must fit in int32.
+  // Segment records and flat tile indices (sequence, KV head, tile) must fit
+  // in int32.
+  if ((int64_t)num_seqs * desc->num_kv_heads * kRecInts >= (1ll << 31))
+    return pa::fail(PA_ERR_UNSUPPORTED, "num_seqs * KV heads too large");
   if ((int64_t)num_seqs * ((len_cap + kTile - 1) / kTile) * desc->num_kv_heads >= (1ll << 31))
     return pa::fail(PA_ERR_UNSUPPORTED, "num_seqs * tiles per sequence * KV heads >= 2^31");
   if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
@@ -1070,7 +1101,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!pa::aligned(q, 16) || !pa::aligned(k_cache, 16) || !pa::aligned(v_cache, 16) ||
       !pa::aligned(out, 16) || !pa::aligned(block_tables, 4) || !pa::aligned(context_lens, 4))
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "misaligned pointer");
-  const WorkspaceLayout wl = workspace_layout(desc, num_q_heads);
+  const WorkspaceLayout wl = workspace_layout(desc, num_q_heads, num_seqs);
   if (workspace_bytes < wl.total)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace %zu bytes < %zu needed", workspace_bytes,
                     wl.total);

@@ -92,12 +92,24 @@ __device__ __forceinline__ float pick_row_quad(float x, int jr) {
   return jr == 0 ? s0 : (jr == 1 ? s1 : (jr == 2 ? s2 : s3));
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+// Integer DPP move: lanes whose source is outside the row (or rows left out
+// of RowMask) read 0.
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ int dpp_or_zero(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, Ctrl, RowMask, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP only (no LDS): shifts by
+// 1, 2, 4 and 8 within each 16-lane row, then row_bcast:15 adds row 0's
+// total to row 1 and row 2's to row 3, and row_bcast:31 adds the total of
+// rows 0-1 to rows 2-3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_or_zero<0x111>(v);       // row_shr:1
+  v += dpp_or_zero<0x112>(v);       // row_shr:2
+  v += dpp_or_zero<0x114>(v);       // row_shr:4
+  v += dpp_or_zero<0x118>(v);       // row_shr:8
+  v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
