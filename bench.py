@@ -63,6 +63,10 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the run, copy a MIB-MiB device buffer 4 times (a plain copy kernel "
                         "of known size, to scale the HBM byte counters of a profiler pass)")
+    p.add_argument("--workload", default="llama3_8b_decode",
+                   help="llama3_8b_decode (the default bench line), or serving_batch, "
+                        "block_size_sweep_bs{8,16,32,128}, prefix_sharing_p{2056,2048}: pa_decode "
+                        "alone on that workload's batch (kernel leg only)")
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying a captured HIP graph")
     return p.parse_args()
@@ -139,6 +143,86 @@ def cpu_baseline(w, seconds):
                       f"in {el:.1f} s, NumPy fp64 paged decode incl. bf16 widening"}
 
 
+def other_workload(args):
+    """pa_decode alone on another workload: the allocator script is replayed
+    on the host (tables and lengths exactly as the workload builds them), the
+    pools of args.layers layers hold random bf16 values (the values do not
+    change the time), and a captured graph of one call per layer is replayed
+    args.kernel_reps times between HIP events."""
+    import torch
+
+    import paged_kv_cache_338_amd as pa
+    import workloads as W
+
+    name = args.workload
+    if name.startswith("block_size_sweep_bs"):
+        w = W.block_size_sweep(int(name[len("block_size_sweep_bs"):]), with_values=False)
+    elif name.startswith("prefix_sharing_p"):
+        w = W.prefix_sharing(prefix_len=int(name[len("prefix_sharing_p"):]), with_values=False)
+    elif name == "serving_batch":
+        w = W.serving_batch(with_values=False)
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    dev = "cuda:0"
+    alloc = pa.Allocator(w.num_blocks, w.block_size, w.free_order)
+    for op in w.script:
+        if op[0] == "create":
+            alloc.seq_create(op[1])
+        elif op[0] == "fork":
+            alloc.seq_fork(op[1], op[2])
+        else:
+            alloc.seq_reserve(op[1], op[2], cow_cap=len(op[1]))
+    maxb = max(len(alloc.seq_block_table(s)) for s in w.seq_ids)
+    tables, lens = alloc.build_block_tables(w.seq_ids, maxb)
+    B, H_q, D = w.batch, w.num_q_heads, w.head_dim
+    shape = (w.num_blocks, w.num_kv_heads, w.block_size, D)
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    kp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(args.layers)]
+    vp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(args.layers)]
+    q = torch.randn((B, H_q, D), generator=gen, device=dev).to(torch.bfloat16)
+    outs = [torch.empty_like(q) for _ in range(args.layers)]
+    ws = pa.decode_workspace(kp[0], B, H_q, maxb)
+    td = torch.from_numpy(tables).to(dev)
+    ld = torch.from_numpy(lens).to(dev)
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        calls = [pa.prepare_decode(q, kp[l], vp[l], td, ld, w.block_size, w.scale, outs[l], ws)
+                 for l in range(args.layers)]
+        for c in calls:
+            c()
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for c in calls:
+                c()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.kernel_reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (args.kernel_reps * args.layers)
+    kv = int(lens.sum()) * kv_bytes_per_token(w)
+    gbs = kv / (us * 1e-6) / 1e9
+    log(f"{name}: B={B} tokens={int(lens.sum())} maxb={maxb}: {us:.2f} us/call, {gbs:.0f} GB/s")
+    print(json.dumps({
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.kernel_reps * args.layers, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: pa_decode alone, {args.layers} layer pools, graph replay",
+                   "batch": B, "tokens": int(lens.sum()), "block_size": w.block_size,
+                   "us_per_call": round(us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_call": kv}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -146,6 +230,11 @@ def main():
               "shards by sequence or KV head with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload != "llama3_8b_decode":
+        if args.layers == 32:
+            args.layers = 2  # each of these batches is larger than the last-level cache
+        other_workload(args)
+        return
     import torch
 
     import paged_kv_cache_338_amd as pa
