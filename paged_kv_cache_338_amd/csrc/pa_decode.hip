@@ -73,7 +73,7 @@ constexpr size_t kMaxLds = 160 * 1024;
 #define PA_DECODE_NW 4  // waves per workgroup
 #endif
 #ifndef PA_DECODE_OCC_STREAM
-#define PA_DECODE_OCC_STREAM 1  // waves per SIMD the streamed path's registers must allow
+#define PA_DECODE_OCC_STREAM 2  // waves per SIMD the streamed bf16 path's registers must allow
 #endif
 #ifndef PA_DECODE_OCC
 #define PA_DECODE_OCC 2  // waves per SIMD the register budget must allow
@@ -528,7 +528,7 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x) {
 template <bool BF16, int D, int GP, int kNW, int NBUF, bool kSmall>
 __global__ void __launch_bounds__(kNW * kWave)
 __attribute__((amdgpu_waves_per_eu(kSmall ? ((BF16 || GP * D < 16 * 128) ? PA_DECODE_OCC : 1)
-                                          : PA_DECODE_OCC_STREAM)))
+                                          : (BF16 ? PA_DECODE_OCC_STREAM : 1))))
 decode_kernel(DecodeArgs a) {
   using Geo = Geometry<BF16, D>;
   constexpr int kWG = kNW * kWave;
