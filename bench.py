@@ -90,18 +90,28 @@ DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_338_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_device.h")]
 
 
+def decode_source_hash():
+    """sha256 of the decode sources with comments and whitespace removed, so
+    that only changes to the code itself invalidate a stored measurement."""
+    import hashlib
+    import re
+    text = "".join(open(f).read() for f in DECODE_SOURCES)
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per pa_decode call from the committed counter summary, or None
-    when the decode sources have changed since the counters were taken."""
-    import hashlib
+    when the decode code has changed since the counters were taken."""
     try:
         text = open(TRAFFIC_FILE).read()
-        src = b"".join(open(f, "rb").read() for f in DECODE_SOURCES)
+        code_hash = decode_source_hash()
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines()
                   if line.startswith(("kernel_source_sha256: ", "traffic_bytes_per_call: ")))
-    if fields.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+    if fields.get("kernel_source_sha256") != code_hash:
         return None
     return int(fields["traffic_bytes_per_call"])
 

@@ -18,22 +18,29 @@
 //    waits for another.
 //  * Each workgroup first copies the context lengths into LDS with their
 //    prefix sums over sequences, so its waves see one consistent snapshot.
-//  * A wave walks its share as pieces, one per segment it meets; each piece
-//    is a branch-free loop over batches of NBUF tiles (all loads of a batch
-//    issued before its first use), with the segment's query rows and
-//    physical block ids fetched ahead.  A segment wholly inside the share
-//    is written out by the wave; a piece of a segment cut by a share
-//    boundary leaves its online-softmax state (max, sum, unnormalised
-//    output) as a partial in the workspace.
+//  * Blocks of >= 16 tokens: a wave walks its share as batches of up to
+//    NBUF tiles; a batch holds the rest of one segment and, if that segment
+//    ends inside it, the start of the next, so crossing a segment boundary
+//    costs no extra round trip.  The block ids of the share are fetched 64
+//    tiles at a time by one vector load (lane i: tile i) and read with
+//    v_readlane a batch ahead; each batch issues its segments' query rows
+//    and all its tile loads before the first use.  Smaller blocks: one
+//    pipelined piece per segment, block ids gathered per lane.
+//  * A segment wholly inside the share is written out by the wave; a piece
+//    of a segment cut by a share boundary leaves its online-softmax state
+//    (max, sum, unnormalised output) as a partial in the workspace.
 //  * A second, small kernel merges the partials of each cut segment (the
-//    wave that holds its first piece leaves a record for it), so there is
-//    no cross-wave synchronisation inside the decode kernel.
+//    wave that holds a segment's first tile writes the segment's record), so
+//    there is no cross-wave synchronisation inside the decode kernel: on
+//    this part, publishing data to other workgroups inside one kernel costs
+//    far more (an L2 writeback per release) than a second launch.
 //  * Per tile (bf16 pools): the K rows of the 16 tokens are the A operand of
 //    a v_mfma_f32_16x16x32_bf16 chain whose B operand is the KV head's G
 //    query rows, so the logits of head g and token 4j+r land in lane 16j+g,
 //    register r.  The probabilities, rounded to bf16, are the A operand of
 //    a v_mfma_f32_16x16x16_bf16 chain against the V rows (D/16 output
-//    column blocks), so the output accumulates in MFMA registers too.
+//    column blocks) and against a ones operand (the softmax sums), so the
+//    output and its normaliser accumulate in MFMA registers.
 //    fp32 pools use v_mfma_f32_16x16x4_f32 for the logits and the VALU for
 //    P*V, with the probabilities broadcast by DPP.
 //  * The running max is raised lazily: only when a logit exceeds it by more
@@ -43,8 +50,9 @@
 //    tile; the padding tiles of the pipeline get a zero-length resource, so
 //    every loop iteration issues the same loads and each use waits only for
 //    its own tile.
-//  * Masked positions (past the context length) are removed by select, so
-//    garbage or NaN in unused slots of a block cannot reach the output.
+//  * Masked positions (past the context length, only in a segment's tail
+//    tile) get weight 0 and their V rows are zeroed, so garbage or NaN in
+//    unused slots of a block cannot reach the output.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -66,7 +74,7 @@ constexpr int kTile = 16;         // tokens per tile (one MFMA row block)
 constexpr int kMaxWaves = 4096;   // the workspace holds partials for this many waves
 constexpr int kDefaultWGs = 256;  // workgroups of the decode grid
 constexpr int kMaxSeqs = 8192;    // lengths snapshot in LDS
-constexpr int kRecInts = 8;       // ints per cut-segment record
+constexpr int kRecInts = 8;       // ints per segment record
 constexpr int kMergeWG = 256;     // threads of the partial-merge kernel
 constexpr size_t kMaxLds = 160 * 1024;
 #ifndef PA_DECODE_NW
