@@ -26,6 +26,8 @@ allocator   block allocator: free stack, per-block reference counts,
 cache_ops   slot-mapped append and whole-block copy (exact bit copies)
 attention   paged single-query attention (gather through the block table),
             contiguous-cache attention, scalar brute force
+prefill     paged multi-query (prefill / chunked prefill) causal attention,
+            a dense masked formulation, scalar brute force
 accounting  the pages' memory arithmetic (bytes per token, slab vs block
             utilisation, tail waste, capacity)
 
