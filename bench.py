@@ -87,7 +87,7 @@ def kv_bytes_per_token(w):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_llama3_8b_batch8_hbm_traffic.txt")
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_338_amd", "csrc", f)
-                  for f in ("pa_decode.hip", "pa_device.h")]
+                  for f in ("pa_decode.hip", "pa_attn_tile.h", "pa_device.h")]
 
 
 def decode_source_hash():

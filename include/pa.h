@@ -152,6 +152,32 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Causal multi-query attention through the block tables: prefill and
+ * chunked prefill [P1 body: prefill allocates and fills a prompt's blocks;
+ * P3 Step 3: the prompt's tokens fill logical blocks mapped to scattered
+ * physical ones; P2 Example: the attention arithmetic is the ordinary one].
+ *
+ * Sequence b holds L = context_lens[b] tokens in the cache, the n_b =
+ * query_start[b+1] - query_start[b] query tokens included (appended first by
+ * pa_cache_append).  Query token i (0 <= i < n_b) is at position
+ * p = L - n_b + i and, for every query head h (KV head h / G):
+ *   out[query_start[b] + i][h] = sum_{t <= p} softmax(s)_t * V(b, t, kvh),
+ *   s_t = scale * dot(q[query_start[b] + i][h], K(b, t, kvh)).
+ * q, out:       device [num_query_tokens][num_q_heads][head_dim], bf16 (the
+ *               pools must be bf16; PA_ERR_UNSUPPORTED otherwise).
+ * query_start:  device int32 [num_seqs + 1], non-decreasing from 0 to
+ *               num_query_tokens (values are clamped into that range; n_b is
+ *               clamped to [0, L]; L to max_blocks_per_seq * block_size).
+ * block_tables, context_lens, block_size, desc: as for pa_decode.
+ * num_seqs at most 8192.  No workspace: one wave computes each (sequence, KV
+ * head, 16-query-row tile) over its whole causal key range.  n_b == 1 for
+ * every sequence is decode.  num_query_tokens == 0 enqueues nothing. */
+pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+                     int32_t num_query_tokens, int32_t block_size, float scale, void* out,
+                     int32_t num_q_heads, const pa_cache_desc* desc, void* stream);
+
 /* Bytes of workspace pa_decode needs for this shape (independent of the
  * lengths' values). */
 pa_status pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,

@@ -69,6 +69,8 @@ SIGNATURES = {
     "pa_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32, _c.c_float, _P, _I32, _PDESC,
                          _P, _c.c_size_t, _P]),
     "pa_decode_workspace_size": (_I32, [_PDESC, _I32, _I32, _I32, _c.POINTER(_c.c_size_t)]),
+    "pa_prefill": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _c.c_float, _P, _I32,
+                          _PDESC, _P]),
     "pa_allocator_create": (_I32, [_I32, _I32, _PI32, _c.POINTER(_P)]),
     "pa_allocator_destroy": (None, [_P]),
     "pa_seq_create": (_I32, [_P, _I64]),
@@ -233,6 +235,35 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale
         int(block_size), float(scale), _dev(out, "out"), H_q, ctypes.byref(desc),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size, scale,
+               out, stream=None):
+    """Causal multi-query attention through the block tables: sequence b's
+    query rows are q[query_start[b]:query_start[b + 1]] (its last n_b cache
+    positions), each attending to the cache up to its own position.
+    q, out [T, H_q, D] bf16; block_tables int32 [B, max_blocks]; context_lens
+    int32 [B]; query_start int32 [B + 1]."""
+    torch = _torch()
+    _same_pool(k_cache, v_cache)
+    desc = cache_desc(k_cache)
+    if q.dim() != 3 or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be [T, H_q, D] of one shape")
+    T, H_q, D = q.shape
+    if D != desc.head_dim or q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise ValueError("q/out must match the pool's head_dim and dtype")
+    if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32
+            or query_start.dtype != torch.int32):
+        raise TypeError("block_tables, context_lens and query_start must be int32")
+    B = context_lens.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start.numel() != B + 1:
+        raise ValueError("block_tables must be [B, max_blocks] and query_start [B + 1]")
+    _check(load_library().pa_prefill(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), B, T,
+        int(block_size), float(scale), _dev(out, "out"), H_q, ctypes.byref(desc), _stream(stream)))
     return out
 
 

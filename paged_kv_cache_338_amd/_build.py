@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libpa.so")
 
 ARCH = "gfx950"
 HOST_SOURCES = ["pa_status.cpp", "pa_allocator.cpp"]
-DEVICE_SOURCES = ["pa_cache_ops.hip", "pa_decode.hip"]
+DEVICE_SOURCES = ["pa_cache_ops.hip", "pa_decode.hip", "pa_prefill.hip"]
 # Packed fp32 VALU instructions are disabled for all device code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

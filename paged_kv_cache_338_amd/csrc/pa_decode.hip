@@ -60,17 +60,27 @@
 #include <cstdlib>
 #include <type_traits>
 
+#include "pa_attn_tile.h"
 #include "pa_device.h"
 #include "pa_internal.h"
 
 namespace {
 
+using pa::bf16x2_t;
 using pa::bf16x8_t;
+using pa::f32x2_t;
 using pa::floatx4_t;
+using pa::Geometry;
+using pa::issue_tile;
+using pa::issue_tile_small;
+using pa::kTile;
 using pa::kWave;
+using pa::MfmaState;
+using pa::s16x4_t;
+using pa::TileRegs;
 using pa::u32x4_t;
-
-constexpr int kTile = 16;         // tokens per tile (one MFMA row block)
+using pa::uni;
+using pa::uniform_ptr;
 constexpr int kMaxWaves = 4096;   // the workspace holds partials for this many waves
 constexpr int kDefaultWGs = 256;  // workgroups of the decode grid
 constexpr int kMaxSeqs = 8192;    // lengths snapshot in LDS
@@ -108,25 +118,8 @@ struct DecodeArgs {
   int32_t G;
   int32_t log2_bs;
   float scale_log2;  // scale * log2(e)
-};
 
-template <bool BF16, int D>
-struct Geometry {
-  static constexpr int kElem = BF16 ? 2 : 4;
-  static constexpr int kRowBytes = D * kElem;
-  static constexpr int kKPieces = kRowBytes / 64;     // 16-byte K pieces per lane per tile
-  static constexpr int kVWords = kRowBytes / 16 / 4;  // 32-bit words of V per lane per token
-  static constexpr int kCols = D / 16;                // output columns per lane
-  static constexpr int kQRegs = BF16 ? kKPieces : 1;  // query as bf16 MFMA operand
-  static constexpr int kQF32 = BF16 ? 1 : kKPieces * 4;
-  static_assert(kRowBytes % 64 == 0, "row must be a multiple of 64 bytes");
-};
-
-template <bool BF16, int D>
-struct TileRegs {
-  using Geo = Geometry<BF16, D>;
-  u32x4_t k[Geo::kKPieces];
-  uint32_t v[4][Geo::kVWords];
+  __device__ pa::KvPool pool() const { return {k_cache, v_cache, num_blocks, H_kv, log2_bs}; }
 };
 
 template <bool BF16, int D, int GP>
@@ -145,8 +138,6 @@ struct WaveState {
       for (int c = 0; c < Geo::kCols; ++c) o[g][c] = 0.f;
   }
 };
-
-__device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // One segment (sequence b, KV head kvh) and its flat tile range [S0, S1).
 struct Seg {
@@ -205,118 +196,6 @@ __device__ __forceinline__ void seg_advance(Seg& s, const int32_t* PB, const int
   s.L = uni(Ls[b]);
 }
 
-// A wave-uniform pointer, moved to SGPRs.
-__device__ __forceinline__ char* uniform_ptr(const char* p) {
-  const uint64_t x = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
-  return reinterpret_cast<char*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// Buffer-resource word 3 for raw dword loads on gfx9-family parts (32-bit
-// data format; a zero format would make every load return zero).
-constexpr int32_t kRsrcWord3 = 0x00020000;
-
-// Issues the K/V loads of tile t of a segment (KV head kvh) whose 16 rows
-// lie in physical block `phys` (blocks of >= 16 tokens).  The rows are read
-// through a buffer resource spanning exactly them; pipeline padding
-// (`valid` false) gets a zero-length resource, so its loads return zeros
-// without touching memory.  Rows past the context length stay inside the
-// block and are masked when consumed.
-template <bool BF16, int D>
-__device__ __forceinline__ void issue_tile(TileRegs<BF16, D>& r, const DecodeArgs& a,
-                                           int32_t phys, int32_t t, int32_t kvh, int lane,
-                                           bool valid) {
-  using Geo = Geometry<BF16, D>;
-  const int bs_log = a.log2_bs;
-  const int32_t bs = 1 << bs_log;
-  const int jr = lane >> 4, c16 = lane & 15;
-  phys = min(max(phys, 0), a.num_blocks - 1);
-  const int64_t off0 =
-      (((int64_t)phys * a.H_kv + kvh) * bs + ((t * kTile) & (bs - 1))) * Geo::kRowBytes;
-  // The resource must live in SGPRs: every input is wave-uniform, and
-  // readfirstlane says so to the compiler (otherwise it wraps each load in
-  // a loop over the distinct values of the resource).
-  const int32_t nrec = uni(valid ? kTile * Geo::kRowBytes : 0);
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(reinterpret_cast<const char*>(a.k_cache) + off0), 0, nrec, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(reinterpret_cast<const char*>(a.v_cache) + off0), 0, nrec, kRsrcWord3);
-  const int32_t ko = (lane & 15) * Geo::kRowBytes + jr * 16;
-#pragma unroll
-  for (int p = 0; p < Geo::kKPieces; ++p)
-    r.k[p] = __builtin_bit_cast(u32x4_t,
-                                __builtin_amdgcn_raw_buffer_load_b128(rk, ko + p * 64, 0, 0));
-  const int32_t vo = (jr * 4) * Geo::kRowBytes + c16 * (Geo::kVWords * 4);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-#pragma unroll
-    for (int h = 0; h < Geo::kVWords; h += 4) {
-      if constexpr (Geo::kVWords >= 4) {
-        const u32x4_t x = __builtin_bit_cast(
-            u32x4_t,
-            __builtin_amdgcn_raw_buffer_load_b128(rv, vo + q * Geo::kRowBytes + h * 4, 0, 0));
-        r.v[q][h + 0] = x[0];
-        r.v[q][h + 1] = x[1];
-        r.v[q][h + 2] = x[2];
-        r.v[q][h + 3] = x[3];
-      } else {
-        const uint2 x = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vo + q * Geo::kRowBytes, 0, 0));
-        r.v[q][0] = x.x;
-        r.v[q][1] = x.y;
-      }
-    }
-  }
-}
-
-// Same for blocks of fewer than 16 tokens: a tile spans nbt = 16 / bs
-// blocks, whose ids are lanes jl*nbt .. jl*nbt + nbt - 1 of phys_v; every
-// lane reads its own rows' blocks.  Rows past the context length L (and
-// padding tiles, whose index the caller clamps) read the last valid token
-// again.
-template <bool BF16, int D>
-__device__ __forceinline__ void issue_tile_small(TileRegs<BF16, D>& r, const DecodeArgs& a,
-                                                 int32_t phys_v, int32_t jl, int32_t t,
-                                                 int32_t kvh, int32_t L, int nbt, int lane) {
-  using Geo = Geometry<BF16, D>;
-  const int bs_log = a.log2_bs;
-  const int32_t bs = 1 << bs_log;
-  const int jr = lane >> 4, c16 = lane & 15;
-  const int32_t src = jl * nbt;
-  const int32_t t0 = t * kTile;
-  auto row_addr = [&](int32_t row, const void* base) -> const char* {
-    const int32_t tok = min(t0 + row, L - 1);
-    const int32_t sub = (tok - t0) >> bs_log;
-    const int32_t phys = min(max(__shfl(phys_v, src + sub), 0), a.num_blocks - 1);
-    return reinterpret_cast<const char*>(base) +
-           (((int64_t)phys * a.H_kv + kvh) * bs + (tok & (bs - 1))) * Geo::kRowBytes;
-  };
-  const char* kp = row_addr(lane & 15, a.k_cache) + jr * 16;
-#pragma unroll
-  for (int p = 0; p < Geo::kKPieces; ++p) r.k[p] = *reinterpret_cast<const u32x4_t*>(kp + p * 64);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const char* vp = row_addr(jr * 4 + q, a.v_cache) + c16 * (Geo::kVWords * 4);
-#pragma unroll
-    for (int h = 0; h < Geo::kVWords; h += 4) {
-      if constexpr (Geo::kVWords >= 4) {
-        u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp + h * 4);
-        r.v[q][h + 0] = x[0];
-        r.v[q][h + 1] = x[1];
-        r.v[q][h + 2] = x[2];
-        r.v[q][h + 3] = x[3];
-      } else {
-        uint2 x = *reinterpret_cast<const uint2*>(vp);
-        r.v[q][0] = x.x;
-        r.v[q][1] = x.y;
-      }
-    }
-  }
-}
-
-// Consumes one tile: logits by MFMA, online softmax per 16-lane row, P*V.
-// t0 = first token of the tile within its sequence, end = context length.
 template <bool BF16, int D, int GP>
 __device__ __forceinline__ void consume_tile(WaveState<BF16, D, GP>& st,
                                              const TileRegs<BF16, D>& r, const u32x4_t* qf,
@@ -387,105 +266,6 @@ __device__ __forceinline__ void consume_tile(WaveState<BF16, D, GP>& st,
   });
 }
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Per-wave state over one piece, bf16 pools (P*V by MFMA).
-//  ref: lane 16j + g: reference max of head g (log2 units), equal in all rows.
-//  l:   lane 16j + c, register r: sum of the (bf16-rounded) weights of head
-//       4j + r, equal in every column c (an MFMA of P against ones).
-//  acc[blk]: lane 16j + c, register r: unnormalised output of head 4j + r at
-//       column (D/16)*c + blk.
-template <int D>
-struct MfmaState {
-  static constexpr int kBlk = D / 16;
-  float ref;
-  floatx4_t l;
-  floatx4_t acc[kBlk];
-
-  __device__ __forceinline__ void reset() {
-    ref = -3.0e38f;
-    l = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < kBlk; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  }
-};
-
-// Consumes one tile (bf16): logits S = K q^T by MFMA (lane 16j + g holds
-// heads g, tokens 4j..4j+3); weights p = 2^(x - ref) against a reference
-// max that is raised (and the accumulators rescaled) only when a logit
-// exceeds it by more than 2^8, so the common tile needs no cross-lane
-// reduction; then O += P V by MFMA with P (heads x tokens) exactly where the
-// logits are and V (tokens x columns) made from the lane's own V rows, and
-// l += P 1 by one more MFMA.  Only a tail tile (past the context length)
-// masks: its logits there become -inf (weight 0) and its V rows there
-// become 0, so garbage or NaN in unused slots cannot leak.  Heads >= G have
-// zero query rows; their rows are computed and never stored.
-template <int D, bool kTail>
-__device__ __forceinline__ void consume_tile_mfma_impl(MfmaState<D>& st,
-                                                       const TileRegs<true, D>& r,
-                                                       const u32x4_t* qf, float scale_log2,
-                                                       int32_t t0, int32_t end, int lane) {
-  using Geo = Geometry<true, D>;
-  constexpr int kBlk = MfmaState<D>::kBlk;
-  const int jr = lane >> 4;
-  floatx4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int p = 0; p < Geo::kKPieces; ++p)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[p]),
-                                                __builtin_bit_cast(bf16x8_t, qf[p]), s, 0, 0, 0);
-  float x[4];
-  bool hi = false;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    x[q] = s[q] * scale_log2;
-    if constexpr (kTail)
-      if (t0 + jr * 4 + q >= end) x[q] = -INFINITY;
-    hi = hi || x[q] > st.ref + 8.f;
-  }
-  if (__ballot(hi) != 0) {  // uniform: raise the reference
-    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mt = pa::rows_max(mt);
-    const float nref = fmaxf(st.ref, mt);
-    const float f = __builtin_amdgcn_exp2f(st.ref - nref);
-    st.ref = nref;
-    pa::static_for<0, 4>([&](auto Q) {
-      constexpr int q = decltype(Q)::value;
-      const float fr = pa::pick_row_quad<q>(f, jr);  // head 4j + q
-      st.l[q] *= fr;
-#pragma unroll
-      for (int b = 0; b < kBlk; ++b) st.acc[b][q] *= fr;
-    });
-  }
-  const f32x2_t p01 = {__builtin_amdgcn_exp2f(x[0] - st.ref), __builtin_amdgcn_exp2f(x[1] - st.ref)};
-  const f32x2_t p23 = {__builtin_amdgcn_exp2f(x[2] - st.ref), __builtin_amdgcn_exp2f(x[3] - st.ref)};
-  const uint32_t a01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t));
-  const uint32_t a23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t));
-  const s16x4_t pa_ = __builtin_bit_cast(s16x4_t, (uint64_t)a01 | ((uint64_t)a23 << 32));
-  uint32_t m01 = 0xFFFFFFFFu, m23 = 0xFFFFFFFFu;
-  if constexpr (kTail) {
-    const int32_t row0 = t0 + jr * 4;
-    m01 = (row0 + 0 < end ? 0x0000FFFFu : 0u) | (row0 + 1 < end ? 0xFFFF0000u : 0u);
-    m23 = (row0 + 2 < end ? 0x0000FFFFu : 0u) | (row0 + 3 < end ? 0xFFFF0000u : 0u);
-  }
-#pragma unroll
-  for (int b = 0; b < kBlk; ++b) {
-    const int w = b >> 1;
-    const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t v01 = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel);
-    uint32_t v23 = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel);
-    if constexpr (kTail) {
-      v01 &= m01;
-      v23 &= m23;
-    }
-    const s16x4_t vb = __builtin_bit_cast(s16x4_t, (uint64_t)v01 | ((uint64_t)v23 << 32));
-    st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_, vb, st.acc[b], 0, 0, 0);
-  }
-  const s16x4_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
-  st.l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_, ones, st.l, 0, 0, 0);
-}
-
 // kSplit: take the unmasked variant for whole tiles (a uniform branch);
 // otherwise always mask (one code copy, for register-tight callers).
 template <int D, bool kSplit>
@@ -493,9 +273,9 @@ __device__ __forceinline__ void consume_tile_mfma(MfmaState<D>& st, const TileRe
                                                   const u32x4_t* qf, float scale_log2,
                                                   int32_t t0, int32_t end, int lane) {
   if (kSplit && t0 + kTile <= end)
-    consume_tile_mfma_impl<D, false>(st, r, qf, scale_log2, t0, end, lane);
+    pa::consume_tile_mfma_impl<D, false>(st, r, qf, scale_log2, t0, end - 1, end, lane);
   else
-    consume_tile_mfma_impl<D, true>(st, r, qf, scale_log2, t0, end, lane);
+    pa::consume_tile_mfma_impl<D, true>(st, r, qf, scale_log2, t0, end - 1, end, lane);
 }
 
 // Loads the G query rows of segment (b, kvh) as the MFMA B operand (lane
@@ -784,7 +564,7 @@ decode_kernel(DecodeArgs a) {
         for (int u = 0; u < NBUF; ++u) {
           int32_t kvh, t;
           slot_tile(bt, u, kvh, t);
-          issue_tile<BF16, D>(buf[u], a, ph[u], t, kvh, lane, u < bt.n);
+          issue_tile<BF16, D>(buf[u], a.pool(), ph[u], t, kvh, lane, u < bt.n);
         }
         const Batch nx = next();
         batch_phys(nx, ph);
@@ -863,7 +643,7 @@ decode_kernel(DecodeArgs a) {
             chunkA = c;
             dB = describe(c + 1);
           }
-          issue_tile_small<BF16, D>(r, a, dA, jj - (c << tpc_log), t0 + jj, s.kvh, s.L, nbt,
+          issue_tile_small<BF16, D>(r, a.pool(), dA, jj - (c << tpc_log), t0 + jj, s.kvh, s.L, nbt,
                                     lane);
         };
         pa::static_for<0, NBUF - 1>([&](auto U) { issue(buf[decltype(U)::value], decltype(U)::value); });

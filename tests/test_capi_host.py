@@ -85,6 +85,29 @@ def test_device_entry_points_validate_on_the_host():
     assert st_ == pa.PA_ERR_INVALID_ARGUMENT and b"misaligned" in lib.pa_last_error()
 
 
+def test_prefill_validates_on_the_host():
+    lib = pa.load_library()
+    d = pa.CacheDesc(16, 16, 8, 128, pa.PA_BF16)
+    p16, p8 = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 8)
+
+    def call(q=p16, bs=16, B=2, T=4, maxb=4, scale=1.0, out=p16, desc=d, tables=p16):
+        return lib.pa_prefill(q, p16, p16, tables, maxb, p16, p16, B, T, bs, scale, out, 32,
+                              ctypes.byref(desc), None)
+
+    f32 = pa.CacheDesc(16, 16, 8, 128, pa.PA_F32)
+    assert call(desc=f32) == pa.PA_ERR_UNSUPPORTED and b"bf16" in lib.pa_last_error()
+    assert call(bs=8) == pa.PA_ERR_INVALID_ARGUMENT and b"block_size" in lib.pa_last_error()
+    assert call(B=-1) == pa.PA_ERR_INVALID_ARGUMENT
+    assert call(maxb=0) == pa.PA_ERR_INVALID_ARGUMENT
+    assert call(B=8193) == pa.PA_ERR_UNSUPPORTED
+    assert call(scale=float("inf")) == pa.PA_ERR_INVALID_ARGUMENT
+    assert call(B=0, q=None) == pa.PA_OK and call(T=0, q=None) == pa.PA_OK  # nothing to do
+    assert call(q=None) == pa.PA_ERR_INVALID_ARGUMENT and b"NULL" in lib.pa_last_error()
+    assert call(out=p8) == pa.PA_ERR_INVALID_ARGUMENT and b"misaligned" in lib.pa_last_error()
+    assert call(tables=ctypes.c_void_p((1 << 20) + 2)) == pa.PA_ERR_INVALID_ARGUMENT
+    assert call(T=2**31 - 1, B=8192) == pa.PA_ERR_UNSUPPORTED and b"too many" in lib.pa_last_error()
+
+
 # ------------------------------------------------------------- allocator
 class _OOB(Exception):
     pass

@@ -1,0 +1,159 @@
+"""Prefill (multi-query, causal) attention: HIP path vs the CPU oracle on the
+same seeded inputs (needs a gfx950 GPU).  bf16 pools, N(0, 1) values,
+max-abs tolerance 2e-2; pools start NaN-poisoned, so any read of an
+unwritten slot (or of a key after a query's position, in a block tail)
+shows up as a non-finite or wrong output."""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import prefill as opf
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+POISON = 0x7FC0  # bf16 NaN
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import paged_kv_cache_338_amd as pa
+    pa.load_library()
+    yield
+
+
+def _case(seed, lengths, nq, G=4, H_kv=2, D=128, bs=16, spare=3):
+    """Pools with shuffled blocks; only each sequence's own token slots hold
+    values, every other slot is NaN."""
+    rng = np.random.default_rng(seed)
+    nblk = [-(-L // bs) for L in lengths]
+    nb = sum(nblk) + spare
+    perm = rng.permutation(nb)
+    tables = np.full((len(lengths), max(max(nblk), 1)), -1, np.int32)
+    k = np.full((nb, H_kv, bs, D), POISON, np.uint16)
+    v = np.full((nb, H_kv, bs, D), POISON, np.uint16)
+    c = 0
+    for b, (L, n) in enumerate(zip(lengths, nblk)):
+        tables[b, :n] = perm[c:c + n]
+        c += n
+        for t in range(L):
+            blk = tables[b, t // bs]
+            k[blk, :, t % bs] = W.round_to_bf16_bits(rng.standard_normal((H_kv, D)).astype(np.float32))
+            v[blk, :, t % bs] = W.round_to_bf16_bits(rng.standard_normal((H_kv, D)).astype(np.float32))
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = W.round_to_bf16_bits(rng.standard_normal((int(qs[-1]), G * H_kv, D)).astype(np.float32))
+    return q, k, v, tables, np.array(lengths, np.int32), qs, bs
+
+
+def _bf16(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def _run(q, k, v, tables, lens, qs, bs, scale):
+    import torch
+    import paged_kv_cache_338_amd as pa
+    dev = "cuda:0"
+    qd = _bf16(q, dev)
+    out = torch.full_like(qd, float("nan"))
+    pa.pa_prefill(qd, _bf16(k, dev), _bf16(v, dev), torch.from_numpy(tables).to(dev),
+                  torch.from_numpy(lens).to(dev), torch.from_numpy(qs).to(dev), bs, scale, out)
+    torch.cuda.synchronize()
+    return out.cpu().to(torch.float64).numpy()
+
+
+def _check(seed, lengths, nq, **kw):
+    q, k, v, t, lens, qs, bs = _case(seed, lengths, nq, **kw)
+    scale = 1.0 / np.sqrt(q.shape[2])
+    got = _run(q, k, v, t, lens, qs, bs, scale)
+    want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "bf16")
+    assert got.shape == want.shape
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - want).max()) if got.size else 0.0
+    assert err <= TOL, err
+    return got
+
+
+SHAPES = [
+    # (G, H_kv, D, bs, lengths, query tokens)
+    (4, 2, 128, 16, [37, 16, 100, 1], [37, 16, 20, 1]),       # whole prompts and a chunk
+    (1, 3, 128, 16, [40, 5], [13, 5]),
+    (2, 2, 64, 8, [70, 9, 130], [70, 2, 33]),
+    (8, 1, 128, 32, [65, 200], [3, 64]),
+    (16, 1, 128, 16, [50, 17], [17, 17]),
+    (3, 2, 128, 16, [51, 29], [11, 29]),                       # G not a power of two
+    (4, 2, 128, 4, [23, 9, 64], [23, 1, 40]),
+    (4, 2, 128, 1, [19, 7], [19, 3]),
+    (4, 2, 128, 128, [300, 129], [100, 129]),
+    (4, 2, 64, 256, [257, 31], [257, 31]),
+    (4, 2, 128, 16, [1000, 3], [200, 3]),                      # many key tiles and chunks
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"G{s[0]}_H{s[1]}_D{s[2]}_bs{s[3]}" for s in SHAPES])
+def test_shapes(shape):
+    G, H_kv, D, bs, lengths, nq = shape
+    _check(sum(lengths) + G, lengths, nq, G=G, H_kv=H_kv, D=D, bs=bs)
+
+
+def test_sequences_without_queries_are_skipped():
+    _check(3, [40, 12, 33, 7], [0, 12, 0, 7])
+
+
+def test_llama_shape_chunked_prefill():
+    # The worked batch's lengths; each sequence prefills its last 64 tokens
+    # (or its whole prompt when shorter): 32 Q / 8 KV heads, head 128, bs 16.
+    lengths = list(W.LLAMA3_8B_BATCH)
+    nq = [min(64, L) for L in lengths]
+    _check(11, lengths, nq, G=4, H_kv=8, D=128, bs=16, spare=0)
+
+
+def test_one_query_token_matches_decode():
+    import torch
+    import paged_kv_cache_338_amd as pa
+    q, k, v, t, lens, qs, bs = _case(12, [33, 90, 5, 200], [1, 1, 1, 1])
+    dev = "cuda:0"
+    scale = 0.088
+    got = _run(q, k, v, t, lens, qs, bs, scale)
+    qd = _bf16(q, dev)
+    out = torch.empty_like(qd)
+    pa.pa_decode(qd, _bf16(k, dev), _bf16(v, dev), torch.from_numpy(t).to(dev),
+                 torch.from_numpy(lens).to(dev), bs, scale, out)
+    torch.cuda.synchronize()
+    dec = out.cpu().to(torch.float64).numpy()
+    assert float(np.abs(got - dec).max()) <= TOL
+
+
+def test_physical_relabelling_is_bit_identical():
+    q, k, v, t, lens, qs, bs = _case(13, [77, 40], [30, 40])
+    a = _run(q, k, v, t, lens, qs, bs, 0.1)
+    rng = np.random.default_rng(14)
+    pi = rng.permutation(k.shape[0])
+    k2, v2 = np.empty_like(k), np.empty_like(v)
+    k2[pi], v2[pi] = k, v
+    t2 = np.where(t >= 0, pi[np.maximum(t, 0)], -1).astype(np.int32)
+    b = _run(q, k2, v2, t2, lens, qs, bs, 0.1)
+    assert np.array_equal(a, b)
+
+
+def test_rejects_f32_pools_and_bad_arguments():
+    import torch
+    import paged_kv_cache_338_amd as pa
+    dev = "cuda:0"
+    kc = torch.zeros((4, 2, 16, 64), dtype=torch.float32, device=dev)
+    q = torch.zeros((3, 4, 64), dtype=torch.float32, device=dev)
+    tab = torch.zeros((1, 2), dtype=torch.int32, device=dev)
+    lens = torch.tensor([3], dtype=torch.int32, device=dev)
+    qs = torch.tensor([0, 3], dtype=torch.int32, device=dev)
+    with pytest.raises(pa.PagedAttentionError) as e:
+        pa.pa_prefill(q, kc, kc, tab, lens, qs, 16, 1.0, torch.empty_like(q))
+    assert e.value.status == pa.PA_ERR_UNSUPPORTED
+    kb = kc.to(torch.bfloat16)
+    qb = q.to(torch.bfloat16)
+    with pytest.raises(TypeError):
+        pa.pa_prefill(qb, kb, kb, tab, lens, qs.long(), 16, 1.0, torch.empty_like(qb))
+    with pytest.raises(ValueError):
+        pa.pa_prefill(qb, kb, kb, tab, lens, qs[:1], 16, 1.0, torch.empty_like(qb))
