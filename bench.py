@@ -66,7 +66,8 @@ def parse():
     p.add_argument("--workload", default="llama3_8b_decode",
                    help="llama3_8b_decode (the default bench line), or serving_batch, "
                         "block_size_sweep_bs{8,16,32,128}, prefix_sharing_p{2056,2048}: pa_decode "
-                        "alone on that workload's batch (kernel leg only)")
+                        "alone on that workload's batch (kernel leg only); llama3_8b_prefill, "
+                        "llama3_8b_chunked_prefill_cN: pa_prefill alone on the worked batch")
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying a captured HIP graph")
     return p.parse_args()
@@ -153,6 +154,51 @@ def cpu_baseline(w, seconds):
                       f"in {el:.1f} s, NumPy fp64 paged decode incl. bf16 widening"}
 
 
+def replay_timed(make_calls, reps):
+    """Captures the prepared calls in one HIP graph (on a side stream, after an
+    eager run) and returns the microseconds per replay over reps replays,
+    timed with HIP events on the current stream."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        calls = make_calls()
+        for c in calls:
+            c()
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for c in calls:
+                c()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def replay_allocator_script(pa, w):
+    """The C++ allocator after the workload's script; its tables and lengths."""
+    alloc = pa.Allocator(w.num_blocks, w.block_size, w.free_order)
+    for op in w.script:
+        if op[0] == "create":
+            alloc.seq_create(op[1])
+        elif op[0] == "fork":
+            alloc.seq_fork(op[1], op[2])
+        else:
+            alloc.seq_reserve(op[1], op[2], cow_cap=len(op[1]))
+    maxb = max(len(alloc.seq_block_table(s)) for s in w.seq_ids)
+    tables, lens = alloc.build_block_tables(w.seq_ids, maxb)
+    return tables, lens, maxb
+
+
 def other_workload(args):
     """pa_decode alone on another workload: the allocator script is replayed
     on the host (tables and lengths exactly as the workload builds them), the
@@ -174,16 +220,7 @@ def other_workload(args):
     else:
         raise SystemExit(f"unknown workload {name}")
     dev = "cuda:0"
-    alloc = pa.Allocator(w.num_blocks, w.block_size, w.free_order)
-    for op in w.script:
-        if op[0] == "create":
-            alloc.seq_create(op[1])
-        elif op[0] == "fork":
-            alloc.seq_fork(op[1], op[2])
-        else:
-            alloc.seq_reserve(op[1], op[2], cow_cap=len(op[1]))
-    maxb = max(len(alloc.seq_block_table(s)) for s in w.seq_ids)
-    tables, lens = alloc.build_block_tables(w.seq_ids, maxb)
+    tables, lens, maxb = replay_allocator_script(pa, w)
     B, H_q, D = w.batch, w.num_q_heads, w.head_dim
     shape = (w.num_blocks, w.num_kv_heads, w.block_size, D)
     gen = torch.Generator(device=dev).manual_seed(w.seed)
@@ -194,29 +231,9 @@ def other_workload(args):
     ws = pa.decode_workspace(kp[0], B, H_q, maxb)
     td = torch.from_numpy(tables).to(dev)
     ld = torch.from_numpy(lens).to(dev)
-    stream = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        calls = [pa.prepare_decode(q, kp[l], vp[l], td, ld, w.block_size, w.scale, outs[l], ws)
-                 for l in range(args.layers)]
-        for c in calls:
-            c()
-        side.synchronize()
-        with torch.cuda.graph(g, stream=side):
-            for c in calls:
-                c()
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.kernel_reps):
-        g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (args.kernel_reps * args.layers)
+    us = replay_timed(lambda: [pa.prepare_decode(q, kp[l], vp[l], td, ld, w.block_size, w.scale,
+                                                 outs[l], ws) for l in range(args.layers)],
+                      args.kernel_reps) / args.layers
     kv = int(lens.sum()) * kv_bytes_per_token(w)
     gbs = kv / (us * 1e-6) / 1e9
     log(f"{name}: B={B} tokens={int(lens.sum())} maxb={maxb}: {us:.2f} us/call, {gbs:.0f} GB/s")
@@ -233,6 +250,129 @@ def other_workload(args):
                      "algorithmic_bytes_per_call": kv}}), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_METRIC = ("paged prefill attention TFLOP/s (% of dense bf16 MFMA peak), Llama-3-8B shape, "
+                  "worked-example batch")
+
+
+def prefill_queries(lens, chunk):
+    """Query tokens per sequence: the whole prompt (chunk None) or its last
+    min(chunk, L_b) tokens (a chunked-prefill step)."""
+    lens = np.asarray(lens, np.int64)
+    return lens.copy() if chunk is None else np.minimum(lens, chunk)
+
+
+def prefill_flops(lens, nq, num_q_heads, head_dim):
+    """Work of one causal call: every (query row, key) pair the mask keeps
+    costs 2*D flops for q.k and 2*D for p.v, per query head."""
+    lens, nq = np.asarray(lens, np.int64), np.asarray(nq, np.int64)
+    pairs = nq * (lens - nq) + nq * (nq + 1) // 2
+    return int(pairs.sum()) * num_q_heads * 4 * head_dim
+
+
+def prefill_workload(args):
+    """pa_prefill alone on the worked batch at the Llama-3-8B shape: the
+    whole prompts (llama3_8b_prefill, 10,578 query tokens) or a chunk of the
+    last N tokens of each (llama3_8b_chunked_prefill_cN).  Tables come from
+    the allocator script; pools of args.layers layers hold random bf16."""
+    import torch
+
+    import paged_kv_cache_338_amd as pa
+    import workloads as W
+
+    name = args.workload
+    if name == "llama3_8b_prefill":
+        chunk = None
+    elif name.startswith("llama3_8b_chunked_prefill_c"):
+        chunk = int(name[len("llama3_8b_chunked_prefill_c"):])
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    dev = "cuda:0"
+    w = W.llama3_8b_decode(with_values=False)
+    tables, lens, maxb = replay_allocator_script(pa, w)
+    nq = prefill_queries(lens, chunk)
+    qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    T, H_q, D = int(qs[-1]), w.num_q_heads, w.head_dim
+    shape = (w.num_blocks, w.num_kv_heads, w.block_size, D)
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    kp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(args.layers)]
+    vp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(args.layers)]
+    q = torch.randn((T, H_q, D), generator=gen, device=dev).to(torch.bfloat16)
+    outs = [torch.empty_like(q) for _ in range(args.layers)]
+    td = torch.from_numpy(tables).to(dev)
+    ld = torch.from_numpy(lens).to(dev)
+    qsd = torch.from_numpy(qs).to(dev)
+    us = replay_timed(lambda: [pa.prepare_prefill(q, kp[l], vp[l], td, ld, qsd, w.block_size,
+                                                  w.scale, outs[l]) for l in range(args.layers)],
+                      args.kernel_reps) / args.layers
+    flops = prefill_flops(lens, nq, H_q, D)
+    tfs = flops / (us * 1e-6) / 1e12
+    log(f"{name}: B={w.batch} query tokens={T} cache tokens={int(lens.sum())}: {us:.2f} us/call, "
+        f"{tfs:.1f} TFLOP/s")
+    result = {
+        "metric": PREFILL_METRIC, "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.kernel_reps * args.layers, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: pa_prefill alone, {args.layers} layer pools, graph replay; "
+                               "32 Q / 8 KV heads, head 128, bs 16, bf16",
+                   "batch": w.batch, "query_tokens": T, "cache_tokens": int(lens.sum()),
+                   "query_tokens_per_seq": nq.tolist(), "us_per_call": round(us, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "pa_prefill (one kernel), one layer",
+                     "us_per_launch": round(us, 3), "algorithmic_flops_per_call": flops},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)...")
+        result["cpu_baseline"] = cpu_baseline_prefill(w.seed, chunk, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_prefill(seed, chunk, seconds):
+    """The oracle's paged prefill on the same batch, one sequence per call in
+    batch order until the time budget is spent (the sample)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import allocator as oa
+    from oracle import cache_ops as oc
+    from oracle import prefill as op
+    import workloads as W
+
+    w = W.llama3_8b_decode(seed=seed)
+    cores = len(os.sched_getaffinity(0))
+    alloc = oa.BlockAllocator(w.num_blocks, w.block_size, w.free_order)
+    kc, vc = w.empty_pool(), w.empty_pool()
+    for o in w.script:
+        if o[0] == "create":
+            alloc.seq_create(o[1])
+        else:
+            slots, _ = alloc.seq_reserve(o[1], o[2])
+            oc.cache_append(kc, vc, w.k_rows[o[3]], w.v_rows[o[3]], slots, w.block_size)
+    maxb = max(len(alloc.seq_block_table(s)) for s in w.seq_ids)
+    rows, lens = alloc.block_tables(w.seq_ids, maxb)
+    tables, lens = np.array(rows, np.int32), np.array(lens, np.int64)
+    nq = prefill_queries(lens, chunk)
+    rng = np.random.default_rng(seed)
+    flops, done, t0 = 0, [], time.perf_counter()
+    with threadpool_limits(limits=cores):
+        for b in range(len(lens)):
+            n = int(nq[b])
+            qb = W.round_to_bf16_bits(rng.standard_normal((n, w.num_q_heads, w.head_dim),
+                                                          dtype=np.float32))
+            op.paged_prefill(qb, kc, vc, tables[b:b + 1], lens[b:b + 1], [0, n], w.block_size,
+                             w.scale, w.dtype)
+            flops += op.prefill_flops(lens[b:b + 1], [0, n], w.num_q_heads, w.head_dim)
+            done.append(n)
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"sequences 0..{len(done) - 1} of the batch (query tokens {done}) in "
+                      f"{el:.1f} s, NumPy fp64 paged prefill incl. bf16 widening"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -243,7 +383,10 @@ def main():
     if args.workload != "llama3_8b_decode":
         if args.layers == 32:
             args.layers = 2  # each of these batches is larger than the last-level cache
-        other_workload(args)
+        if "prefill" in args.workload:
+            prefill_workload(args)
+        else:
+            other_workload(args)
         return
     import torch
 

@@ -245,6 +245,14 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, blo
     positions), each attending to the cache up to its own position.
     q, out [T, H_q, D] bf16; block_tables int32 [B, max_blocks]; context_lens
     int32 [B]; query_start int32 [B + 1]."""
+    prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size,
+                    scale, out, stream)()
+    return out
+
+
+def prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size,
+                    scale, out, stream=None):
+    """pa_prefill with its arguments checked and fixed (see pa_prefill)."""
     torch = _torch()
     _same_pool(k_cache, v_cache)
     desc = cache_desc(k_cache)
@@ -259,12 +267,14 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, blo
     B = context_lens.numel()
     if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start.numel() != B + 1:
         raise ValueError("block_tables must be [B, max_blocks] and query_start [B + 1]")
-    _check(load_library().pa_prefill(
-        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(block_tables, "block_tables"), block_tables.shape[1],
-        _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), B, T,
-        int(block_size), float(scale), _dev(out, "out"), H_q, ctypes.byref(desc), _stream(stream)))
-    return out
+    lib = load_library()
+    args = (_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(block_tables, "block_tables"), block_tables.shape[1],
+            _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), B, T,
+            int(block_size), ctypes.c_float(scale), _dev(out, "out"), H_q, ctypes.byref(desc),
+            _stream(stream))
+    return PreparedCall(lib.pa_prefill, args, (q, k_cache, v_cache, block_tables, context_lens,
+                                               query_start, out, desc))
 
 
 # --------------------------------------------------------------- allocator

@@ -11,19 +11,22 @@
 // tokens are the last n_b, the i-th at position L_b - n_b + i, and attends to
 // positions 0..L_b - n_b + i (causal).
 //
-// Work decomposition: a work item is one (sequence, KV head, query tile):
-// 16 query rows, i.e. 16 / GP tokens x the GP heads of the KV head's group
-// (GP = G rounded up to a power of two; rows of heads >= G are padding).
-// One wave takes one item and walks its whole causal key range, 16 keys per
-// tile, in batches of NBUF tiles whose loads are all issued before the first
-// use.  Items of a sequence are ordered longest first, so the long ones
-// start early and the hardware scheduler back-fills the rest.
+// Work decomposition: a workgroup takes one (sequence, KV head, query
+// block): 4 waves x R row blocks x 16 rows, a row being one (query token,
+// head of the KV head's group) pair, GP heads per token (G rounded up to a
+// power of two; rows of heads >= G are padding).  Query blocks of a sequence
+// are ordered longest first.  The workgroup walks the keys of its causal
+// range in tiles of 32: the 256 threads gather a tile's K and V rows through
+// the block table into registers (one tile ahead, with the table entries
+// read one tile earlier still), store them to a double-buffered, padded LDS
+// tile, and every wave then computes its rows against it.  So each K/V byte
+// crosses the cache hierarchy once per 64 R rows, not once per 16.
 //
-// Per tile: S = K Q^T by v_mfma_f32_16x16x32_bf16 (A = 16 K rows, B = the
-// 16 query rows), the lazily rescaled online softmax, and O += P V, l += P 1
-// by v_mfma_f32_16x16x16_bf16; the step is the decode kernel's, with a
-// causal limit per query row.  Only tiles that cross the diagonal of the
-// item's first query token mask anything.
+// Per tile and row block, on the MFMA units (v_mfma_f32_16x16x32_bf16
+// throughout): S = K Q^T (two 16-key blocks), the lazily rescaled online
+// softmax of the decode kernel, then O += P V and l += P 1 with the 32 keys
+// as the contraction.  Only the tiles that cross a wave's first diagonal
+// mask anything; K/V rows past the cache length are loaded as zeros.
 //
 // The query rows need MFMA operands in bf16, so the call takes bf16 pools
 // only.
@@ -40,22 +43,22 @@
 namespace {
 
 using pa::bf16x2_t;
+using pa::bf16x8_t;
 using pa::f32x2_t;
 using pa::floatx4_t;
-using pa::Geometry;
-using pa::kTile;
 using pa::kWave;
-using pa::MfmaState;
-using pa::TileRegs;
 using pa::u32x4_t;
 using pa::uni;
 
-constexpr int kNW = 4;              // waves per workgroup (one work item each)
-constexpr int kMaxSeqs = 8192;      // query starts and lengths snapshot in LDS
-constexpr int kChunk = 64;          // table lanes per block-id chunk
-#ifndef PA_PREFILL_NB
-#define PA_PREFILL_NB 4             // tiles per batch (divides every chunk)
-#endif
+constexpr int kNW = 4;          // waves per workgroup
+constexpr int kThreads = kNW * kWave;
+constexpr int kMaxSeqs = 8192;  // query starts and lengths snapshot in LDS
+constexpr int kKT = 32;         // keys per LDS tile
+constexpr int kOcc = 2;         // waves per SIMD the registers are sized for
+// Row blocks per wave: 2 normally, 1 when that leaves too few workgroups
+// to fill the chip (measured on the Llama-3-8B shape: R = 2 is faster from
+// about two workgroups per CU up, R = 1 below).
+constexpr int64_t kMinItemsR2 = 512;
 
 struct PrefillArgs {
   const void* q;            // [T][H_q][D]
@@ -71,6 +74,21 @@ struct PrefillArgs {
   float scale_log2;         // scale * log2(e)
 };
 
+template <int D>
+struct TileGeo {
+  static constexpr int kRowBytes = D * 2;
+  // LDS rows padded to 1.5x: the fastest of the paddings measured (bank
+  // conflict cycles fall to a half of the 16-byte padding's).
+  static constexpr int kRowLds = kRowBytes + kRowBytes / 2;
+  static constexpr int kMat = kKT * kRowLds;           // one K or V tile in LDS
+  static constexpr int kStage = 2 * kMat;              // K then V
+  static constexpr int kPPR = kRowBytes / 16;          // 16-byte pieces per row
+  static constexpr int kLoads = kKT * kPPR / kThreads; // pieces per thread per matrix
+  static constexpr int kDS = D / 32;                   // QK contraction slices
+  static constexpr int kBlk = D / 16;                  // output columns per lane
+  static_assert(kLoads >= 1 && kKT * kPPR % kThreads == 0, "tile must split over the threads");
+};
+
 // Largest b in [0, B) with P[b] * H <= f (P: exclusive prefix sums in LDS).
 __device__ __forceinline__ int32_t find_item_seq(const int32_t* P, int32_t B, int32_t H,
                                                  int32_t f) {
@@ -83,28 +101,31 @@ __device__ __forceinline__ int32_t find_item_seq(const int32_t* P, int32_t B, in
   return lo;
 }
 
-template <int D, int GP, bool kSmall>
-__global__ void __launch_bounds__(kNW * kWave)
+template <int D, int GP, int R>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kOcc, kOcc)))
 prefill_kernel(PrefillArgs a) {
-  using Geo = Geometry<true, D>;
-  constexpr int kBlk = D / 16;
-  constexpr int TP = kTile / GP;  // query tokens per work item
-  constexpr int NBUF = PA_PREFILL_NB;
+  using Geo = TileGeo<D>;
+  constexpr int kBlk = Geo::kBlk, kDS = Geo::kDS, kLoads = Geo::kLoads;
+  constexpr int TP = 16 / GP;          // query tokens per 16-row block
+  constexpr int QW = R * TP;           // query tokens per wave
+  constexpr int QT = kNW * QW;         // query tokens per workgroup
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), v = tid >> 6;
   const int jr = lane >> 4, c16 = lane & 15;
   const int32_t B = a.B, H_kv = a.pool.H_kv, G = a.G, H_q = H_kv * G;
   const int log2_bs = a.pool.log2_bs;
+  const int32_t len_cap = a.max_blocks << log2_bs;
 
   // LDS: per sequence the query start, the number of query tokens n_b
-  // (clamped to [0, L_b]) and the exclusive prefix sums of its tiles.
+  // (clamped to [0, L_b]) and the exclusive prefix sums of its query
+  // blocks; then the two K/V tile stages.
   int32_t* QS = reinterpret_cast<int32_t*>(smem);  // [B]
   int32_t* NQ = QS + B;                            // [B]
   int32_t* PQ = NQ + B;                            // [B + 1]
   int32_t* misc = PQ + B + 1;                      // [kNW]
-  const int32_t len_cap = a.max_blocks << log2_bs;
+  char* tiles = smem + (((3 * B + 1 + kNW) * 4 + 15) & ~15);
   int32_t carry = 0;
-  for (int32_t c = 0; c < B; c += kNW * kWave) {
+  for (int32_t c = 0; c < B; c += kThreads) {
     const int32_t b = c + tid;
     int32_t nt = 0;
     if (b < B) {
@@ -114,7 +135,7 @@ prefill_kernel(PrefillArgs a) {
       const int32_t n = min(q1 - q0, L);
       QS[b] = q0;
       NQ[b] = n;
-      nt = (n + TP - 1) / TP;
+      nt = (n + QT - 1) / QT;
     }
     const int32_t incl = pa::wave_incl_scan(nt);
     if (lane == kWave - 1) misc[v] = incl;
@@ -133,132 +154,350 @@ prefill_kernel(PrefillArgs a) {
   if (tid == 0) PQ[B] = carry;
   __syncthreads();
 
-  // ---- this wave's work item: (b, kvh, query tile qt), longest first
+  // ---- this workgroup's item: (b, kvh, query block qb), longest first
   const int32_t items = uni(PQ[B]) * H_kv;
-  const int32_t f = blockIdx.x * kNW + v;
-  if (f >= items) return;
+  const int32_t f = blockIdx.x;
+  if (f >= items) return;  // the whole workgroup
   const int32_t b = uni(find_item_seq(PQ, B, H_kv, f));
   const int32_t local = f - uni(PQ[b]) * H_kv;
   const int32_t kvh = local % H_kv;
   const int32_t nq = uni(NQ[b]);
-  const int32_t nqt = (nq + TP - 1) / TP;
-  const int32_t qt = nqt - 1 - local / H_kv;
-  const int32_t L = min(max(a.lens[b], 0), len_cap);  // wave-uniform (scalar load)
-  const int32_t i0 = qt * TP, i1 = min(i0 + TP, nq);  // query tokens [i0, i1)
+  const int32_t qb = (nq + QT - 1) / QT - 1 - local / H_kv;
+  const int32_t L = min(max(a.lens[b], 0), len_cap);  // uniform (scalar load)
   const int32_t pbase = L - nq;                        // position of query token 0
-  const int32_t p_min = pbase + i0, p_max = pbase + i1 - 1;
-  const int32_t nkv = (p_max + kTile) / kTile;          // key tiles 0 .. p_max
+  const int32_t i0 = qb * QT, i1 = min(i0 + QT, nq);   // the workgroup's tokens
+  const int32_t ntiles = (pbase + i1 - 1) / kKT + 1;   // keys 0 .. its last position
+  // This wave's tokens [w0, w1) and positions.
+  const int32_t w0 = i0 + v * QW, w1 = min(w0 + QW, i1);
+  const bool wave_live = w0 < w1;
+  const int32_t wp_min = pbase + w0, wp_max = pbase + w1 - 1;
 
-  // Query rows: lane c16 is row c16 = (token i0 + c16 / GP, head c16 % GP);
-  // padding rows (past the item's tokens, or heads >= G) are zero.
-  const int32_t row_i = i0 + c16 / GP, row_g = c16 % GP;
-  const bool row_live = row_i < i1 && row_g < G;
-  const int32_t lim = row_live ? pbase + row_i : p_max;  // causal limit of this lane's row
-  u32x4_t qf[Geo::kQRegs];
+  // Query rows: row block r, lane c16 is row c16 = (token w0 + r*TP + c16/GP,
+  // head c16 % GP); padding rows are zero and take the wave's last position
+  // as their causal limit.
+  // A negative scale is applied as |scale| to the negated query (an exact
+  // sign flip in bf16), so that the largest score is the largest logit.
+  const float scale = fabsf(a.scale_log2);
+  const uint32_t qsign_w = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+  const u32x4_t qsign = {qsign_w, qsign_w, qsign_w, qsign_w};
+  u32x4_t qf[R][kDS];
+  int32_t lim[R];
   {
     const int32_t qs_b = uni(QS[b]);
-    const int64_t row = ((int64_t)(qs_b + (row_live ? row_i : i0)) * H_q + kvh * G +
-                         (row_live ? row_g : 0));
-    const char* qb = reinterpret_cast<const char*>(a.q) + row * Geo::kRowBytes + jr * 16;
 #pragma unroll
-    for (int p = 0; p < Geo::kKPieces; ++p) {
-      u32x4_t x = *reinterpret_cast<const u32x4_t*>(qb + p * 64);
-      qf[p] = row_live ? x : u32x4_t{0, 0, 0, 0};
+    for (int r = 0; r < R; ++r) {
+      const int32_t ti = w0 + r * TP + c16 / GP, g = c16 % GP;
+      const bool live = ti < w1 && g < G;
+      lim[r] = live ? pbase + ti : wp_max;
+      const int64_t row = (int64_t)(qs_b + (live ? ti : 0)) * H_q + kvh * G + (live ? g : 0);
+      const char* qp = reinterpret_cast<const char*>(a.q) + row * Geo::kRowBytes + jr * 16;
+#pragma unroll
+      for (int ds = 0; ds < kDS; ++ds) {
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(qp + ds * 64);
+        qf[r][ds] = live ? (x ^ qsign) : u32x4_t{0, 0, 0, 0};
+      }
     }
   }
 
-  // ---- block ids, one chunk of kChunk table lanes ahead: lane i of the
-  // chunk holding tile kt describes tile tpc * c + i / nbt, sub-block
-  // i % nbt (nbt = table lanes per tile).  Entries are clamped into the row.
-  const int nbt = log2_bs >= 4 ? 1 : (kTile >> log2_bs);
-  const int tpc_log = log2_bs >= 4 ? 6 : 2 + log2_bs;  // log2(tiles per chunk)
+  // ---- K/V tile gather: thread tid moves pieces tid + 256 h (row
+  // piece / kPPR, 16-byte column piece % kPPR) of each matrix.
   const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
-  auto describe = [&](int32_t c) -> int32_t {
-    const int32_t kt = min((c << tpc_log) + lane / nbt, nkv - 1);
-    const int32_t tok = min(kt * kTile + ((lane & (nbt - 1)) << log2_bs), L - 1);
-    return trow[min(tok >> log2_bs, a.max_blocks - 1)];
-  };
-  int32_t cur = describe(0), nxt = describe(1);
-  int32_t cur_c = 0;
-
-  MfmaState<D> st;
-  st.reset();
-  for (int32_t k0 = 0; k0 < nkv; k0 += NBUF) {
-    // A batch never straddles a chunk (NBUF divides the tiles per chunk).
-    const int32_t c = k0 >> tpc_log;
-    if (c != cur_c) {
-      cur = nxt;
-      cur_c = c;
-      nxt = describe(c + 1);
-    }
-    TileRegs<true, D> buf[NBUF];
+  const int32_t bs_mask = (1 << log2_bs) - 1;
+  const char* kbase = reinterpret_cast<const char*>(a.pool.k_cache);
+  const char* vbase = reinterpret_cast<const char*>(a.pool.v_cache);
+  auto table_entries = [&](int32_t kt, int32_t (&tb)[kLoads]) {
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
-      const int32_t kt = min(k0 + u, nkv - 1);
-      const int32_t jl = kt - (c << tpc_log);
-      if constexpr (kSmall) {
-        pa::issue_tile_small<true, D>(buf[u], a.pool, cur, jl, kt, kvh, L, nbt, lane);
-      } else {
-        const int32_t phys = __builtin_amdgcn_readlane(cur, jl);
-        pa::issue_tile<true, D>(buf[u], a.pool, phys, kt, kvh, lane, k0 + u < nkv);
+    for (int h = 0; h < kLoads; ++h) {
+      const int32_t key = min(kt * kKT + (tid + h * kThreads) / Geo::kPPR, L - 1);
+      tb[h] = trow[min(key >> log2_bs, a.max_blocks - 1)];
+    }
+  };
+  auto gather = [&](int32_t kt, const int32_t (&tb)[kLoads], u32x4_t (&kr)[kLoads],
+                    u32x4_t (&vr)[kLoads]) {
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h) {
+      const int p = tid + h * kThreads;
+      const int32_t key = kt * kKT + p / Geo::kPPR;
+      const int32_t phys = min(max(tb[h], 0), a.pool.num_blocks - 1);
+      const int64_t off =
+          ((((int64_t)phys * H_kv + kvh) << log2_bs) + (min(key, L - 1) & bs_mask)) *
+              Geo::kRowBytes + (p % Geo::kPPR) * 16;
+      // Every lane loads (the row is clamped into the cache), so the number
+      // of loads in flight is the same on every path; stash zeroes the rows
+      // past the cache.
+      kr[h] = *reinterpret_cast<const u32x4_t*>(kbase + off);
+      vr[h] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+    }
+  };
+  auto stash = [&](int32_t kt, int stage, const u32x4_t (&kr)[kLoads],
+                   const u32x4_t (&vr)[kLoads]) {
+    char* kt_l = tiles + stage * Geo::kStage;
+#pragma unroll
+    for (int h = 0; h < kLoads; ++h) {
+      const int p = tid + h * kThreads;
+      const int o = (p / Geo::kPPR) * Geo::kRowLds + (p % Geo::kPPR) * 16;
+      const bool in = kt * kKT + p / Geo::kPPR < L;  // rows past the cache are zeros
+      *reinterpret_cast<u32x4_t*>(kt_l + o) = in ? kr[h] : u32x4_t{0, 0, 0, 0};
+      *reinterpret_cast<u32x4_t*>(kt_l + Geo::kMat + o) = in ? vr[h] : u32x4_t{0, 0, 0, 0};
+    }
+  };
+
+  // ---- per-row-block softmax state (the decode kernel's conventions):
+  //  ref[r]: lane 16j + c: reference max of row c (log2 units); thr[r] the
+  //  raw score above which a logit exceeds ref[r] + 8;
+  //  l[r], acc[r][blk]: lane 16j + c, register q: row 4j + q; acc at
+  //  column kBlk * c + blk.
+  float ref[R], thr[R];
+  floatx4_t l[R];
+  floatx4_t acc[R][kBlk];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    ref[r] = -3.0e38f;
+    thr[r] = -3.0e38f;
+    l[r] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kBlk; ++k) acc[r][k] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const float inv_scale = scale > 0.f ? 1.f / scale : 0.f;
+  const bf16x8_t ones = __builtin_bit_cast(
+      bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+
+  // Raw scores of a tile: s[kb][r], lane 16j + c, register q = key
+  // t0 + 16 kb + 4j + q against row c of block r; masked keys are -inf.
+  floatx4_t s[2][R];
+  auto front = [&](int stage, int32_t t0, bool masked) -> bool {
+    const char* Kl = tiles + stage * Geo::kStage;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) s[kb][r] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < kDS; ++ds) {
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(
+            Kl + (kb * 16 + c16) * Geo::kRowLds + ds * 64 + jr * 16);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          s[kb][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, kf), __builtin_bit_cast(bf16x8_t, qf[r][ds]),
+              s[kb][r], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    pa::static_for<0, NBUF>([&](auto U) {
-      constexpr int u = decltype(U)::value;
-      const int32_t t0 = (k0 + u) * kTile;
-      if (k0 + u < nkv) {
-        if (t0 + kTile - 1 <= p_min)  // every key at or before every live row
-          pa::consume_tile_mfma_impl<D, false>(st, buf[u], qf, a.scale_log2, t0, lim, L, lane);
-        else
-          pa::consume_tile_mfma_impl<D, true>(st, buf[u], qf, a.scale_log2, t0, lim, L, lane);
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (t0 + kb * 16 + 4 * jr + q > lim[r]) s[kb][r][q] = -INFINITY;
+    }
+    bool hi = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float m = fmaxf(fmaxf(fmaxf(s[0][r][0], s[0][r][1]), fmaxf(s[0][r][2], s[0][r][3])),
+                            fmaxf(fmaxf(s[1][r][0], s[1][r][1]), fmaxf(s[1][r][2], s[1][r][3])));
+      hi = hi || m > thr[r];
+    }
+    return __ballot(hi) != 0;
+  };
+  // Raises the references to the tile's row maxima (where larger) and
+  // rescales l and acc: the only place that touches them outside an MFMA.
+  auto rescale = [&]() {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float m = fmaxf(fmaxf(fmaxf(s[0][r][0], s[0][r][1]), fmaxf(s[0][r][2], s[0][r][3])),
+                      fmaxf(fmaxf(s[1][r][0], s[1][r][1]), fmaxf(s[1][r][2], s[1][r][3])));
+      m = pa::rows_max(m) * scale;
+      const float nref = fmaxf(ref[r], m);
+      const float fac = __builtin_amdgcn_exp2f(ref[r] - nref);
+      ref[r] = nref;
+      thr[r] = (nref + 8.f) * inv_scale;
+      pa::static_for<0, 4>([&](auto Q) {
+        constexpr int q = decltype(Q)::value;
+        const float fr = pa::pick_row_quad<q>(fac, jr);  // row 4j + q
+        l[r][q] *= fr;
+#pragma unroll
+        for (int k = 0; k < kBlk; ++k) acc[r][k][q] *= fr;
+      });
+    }
+  };
+  // p = 2^(score * scale - ref) as the 32-deep operand (the lane's keys
+  // 4j..4j+3, then 16+4j..16+4j+3), l += P 1, O += P V.
+  auto back = [&](int stage) {
+    const char* Vl = tiles + stage * Geo::kStage + Geo::kMat;
+    u32x4_t pp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float nr = -ref[r];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const f32x2_t p01 = {__builtin_amdgcn_exp2f(fmaf(s[kb][r][0], scale, nr)),
+                             __builtin_amdgcn_exp2f(fmaf(s[kb][r][1], scale, nr))};
+        const f32x2_t p23 = {__builtin_amdgcn_exp2f(fmaf(s[kb][r][2], scale, nr)),
+                             __builtin_amdgcn_exp2f(fmaf(s[kb][r][3], scale, nr))};
+        pp[r][2 * kb] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t));
+        pp[r][2 * kb + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t));
+      }
+      l[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pp[r]), ones,
+                                                     l[r], 0, 0, 0);
+    }
+    // V rows 4j + q and 16 + 4j + q, columns kBlk * c .. kBlk * c + kBlk - 1.
+    uint32_t vw[2][4][kBlk / 2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const char* vp = Vl + (kb * 16 + 4 * jr + q) * Geo::kRowLds + c16 * (kBlk * 2);
+        if constexpr (kBlk == 8) {
+          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) vw[kb][q][w] = x[w];
+        } else {
+          const uint2 x = *reinterpret_cast<const uint2*>(vp);
+          vw[kb][q][0] = x.x;
+          vw[kb][q][1] = x.y;
+        }
+      }
+    }
+    // For column group blk the lane's operand is V[key][kBlk*c+blk] over
+    // its 8 keys, in P's key order.
+#pragma unroll
+    for (int k = 0; k < kBlk; ++k) {
+      const int w = k >> 1;
+      const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
+      const u32x4_t vb = {__builtin_amdgcn_perm(vw[0][1][w], vw[0][0][w], sel),
+                          __builtin_amdgcn_perm(vw[0][3][w], vw[0][2][w], sel),
+                          __builtin_amdgcn_perm(vw[1][1][w], vw[1][0][w], sel),
+                          __builtin_amdgcn_perm(vw[1][3][w], vw[1][2][w], sel)};
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        acc[r][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, pp[r]), __builtin_bit_cast(bf16x8_t, vb), acc[r][k],
+            0, 0, 0);
+    }
+  };
+
+  // ---- the key loop, two tiles of loads in flight: at tile kt the
+  // registers of set kt & 1 hold tile kt (stored to LDS stage kt & 1, then
+  // reloaded with tile kt + 2) and the other set holds tile kt + 1.  The
+  // table entries of a tile are read before the gather of the tile before
+  // it, so waiting for them never waits for that gather (loads complete in
+  // order).  A tile whose logits exceed a reference leaves the inner loop
+  // (after its one barrier, like every tile) to be rescaled and finished
+  // outside it, so the hot loop touches the accumulators only through MFMA.
+  int32_t tb[2][kLoads];
+  u32x4_t kr[2][kLoads], vr[2][kLoads];
+  // Tiles past the last are gathered too (clamped, never used): the loads
+  // are unconditional so that the waits stay exact.
+  table_entries(0, tb[0]);
+  table_entries(1, tb[1]);
+  gather(0, tb[0], kr[0], vr[0]);
+  table_entries(2, tb[0]);
+  gather(1, tb[1], kr[1], vr[1]);
+  // One tile: returns true when it must be rescaled (its scores in s).
+  auto step = [&](int32_t kt, auto kSet) -> bool {
+    constexpr int x = decltype(kSet)::value, y = 1 - x;
+    stash(kt, x, kr[x], vr[x]);
+    table_entries(kt + 3, tb[y]);
+    gather(kt + 2, tb[x], kr[x], vr[x]);
+    pa::lds_barrier();
+    const int32_t t0 = kt * kKT;
+    if (wave_live && t0 <= wp_max) {
+      if (front(x, t0, t0 + kKT - 1 > wp_min)) return true;
+      back(x);
+    }
+    return false;
+  };
+  // Tiles go in pairs (set 0, set 1), so the two register sets keep their
+  // registers across iterations; the count is rounded up to even (a spare
+  // last tile computes nothing), and every wave passes exactly one barrier
+  // per tile on every path.
+  const int32_t nt2 = (ntiles + 1) & ~1;
+  const auto set0 = std::integral_constant<int, 0>{};
+  const auto set1 = std::integral_constant<int, 1>{};
+  int32_t kt = 0;
+  while (true) {
+    int brk = -1;  // the set of the tile to rescale, if any
+    if ((kt & 1) && kt < nt2) {  // back from a rescale at an even tile
+      if (step(kt, set1)) brk = 1;
+      else ++kt;
+    }
+    if (brk < 0) {
+      for (; kt < nt2; kt += 2) {
+        if (step(kt, set0)) {
+          brk = 0;
+          break;
+        }
+        if (step(kt + 1, set1)) {
+          brk = 1;
+          ++kt;
+          break;
+        }
+      }
+    }
+    if (brk < 0) break;
+    rescale();
+    back(brk);
+    ++kt;
+  }
+
+  // ---- finish: row block r, lane 16j + c, register q holds row 4j + q at
+  // columns kBlk * c .. kBlk * c + kBlk - 1; its normaliser is l[r][q].
+  if (!wave_live) return;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    pa::static_for<0, 4>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      const int row = 4 * jr + q;
+      const int32_t ti = w0 + r * TP + row / GP, g = row % GP;
+      if (ti < w1 && g < G) {
+        const float inv = 1.f / l[r][q];
+        uint32_t pk[kBlk / 2];
+#pragma unroll
+        for (int k = 0; k < kBlk / 2; ++k) {
+          const f32x2_t pr = {acc[r][2 * k][q] * inv, acc[r][2 * k + 1][q] * inv};
+          pk[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+        }
+        char* dst = reinterpret_cast<char*>(a.out) +
+                    (((int64_t)(uni(QS[b]) + ti) * H_q + kvh * G + g) * D + kBlk * c16) * 2;
+        if constexpr (kBlk == 8) *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+        else *reinterpret_cast<uint2*>(dst) = uint2{pk[0], pk[1]};
       }
     });
   }
-
-  // ---- finish: lane 16j + c, register r holds row 4j + r, columns
-  // kBlk * c .. kBlk * c + kBlk - 1; its normaliser is st.l[r].
-  pa::static_for<0, 4>([&](auto R) {
-    constexpr int r = decltype(R)::value;
-    const int row = 4 * jr + r;
-    const int32_t i = i0 + row / GP, g = row % GP;
-    if (i < i1 && g < G) {
-      const float inv = 1.f / st.l[r];
-      uint32_t pk[kBlk / 2];
-#pragma unroll
-      for (int k = 0; k < kBlk / 2; ++k) {
-        const f32x2_t pr = {st.acc[2 * k][r] * inv, st.acc[2 * k + 1][r] * inv};
-        pk[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
-      }
-      char* dst = reinterpret_cast<char*>(a.out) +
-                  (((int64_t)(uni(QS[b]) + i) * H_q + kvh * G + g) * D + kBlk * c16) * 2;
-      if constexpr (kBlk == 8) *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
-      else *reinterpret_cast<uint2*>(dst) = uint2{pk[0], pk[1]};
-    }
-  });
 }
 
-template <int D, int GP>
-pa_status launch(const PrefillArgs& a, hipStream_t s) {
-  constexpr int TP = kTile / GP;
-  auto kern = a.pool.log2_bs >= 4 ? prefill_kernel<D, GP, false> : prefill_kernel<D, GP, true>;
-  // Work items: at most ceil(T / TP) + B query tiles per KV head; the kernel
-  // numbers them in int32.
-  const int64_t items = (((int64_t)a.T + TP - 1) / TP + a.B) * a.pool.H_kv;
-  if (items + kNW >= (1ll << 31))
-    return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: too many query tiles");
-  const int64_t wgs = (items + kNW - 1) / kNW;
-  const size_t lds = (size_t)(3 * a.B + 1 + kNW) * sizeof(int32_t);
+template <int D, int GP, int R>
+pa_status launch_r(const PrefillArgs& a, int64_t items, hipStream_t s) {
+  auto kern = prefill_kernel<D, GP, R>;
+  const size_t lds = (((size_t)(3 * a.B + 1 + kNW) * 4 + 15) & ~(size_t)15) +
+                     2 * TileGeo<D>::kStage;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess)
       return pa::fail(PA_ERR_DEVICE, "pa_prefill: LDS attribute: %s", hipGetErrorString(e));
   }
-  hipLaunchKernelGGL(kern, dim3((uint32_t)wgs), dim3(kNW * kWave), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3((uint32_t)items), dim3(kThreads), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_DEVICE, "pa_prefill: %s", hipGetErrorString(e));
   return PA_OK;
+}
+
+// Work items for R row blocks per wave: at most ceil(T / QT) + B query
+// blocks per KV head (QT = 4 waves x R x 16 / GP tokens).
+inline int64_t prefill_items(const PrefillArgs& a, int GP, int R) {
+  const int64_t QT = (int64_t)kNW * R * (16 / GP);
+  return (((int64_t)a.T + QT - 1) / QT + a.B) * a.pool.H_kv;
+}
+
+template <int D, int GP>
+pa_status launch(const PrefillArgs& a, hipStream_t s) {
+  const int64_t items1 = prefill_items(a, GP, 1), items2 = prefill_items(a, GP, 2);
+  if (items1 >= (1ll << 31))  // the kernel numbers items in int32
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: too many query blocks");
+  if (items2 >= kMinItemsR2) return launch_r<D, GP, 2>(a, items2, s);
+  return launch_r<D, GP, 1>(a, items1, s);
 }
 
 template <int D>

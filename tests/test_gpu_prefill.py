@@ -65,9 +65,12 @@ def _run(q, k, v, tables, lens, qs, bs, scale):
     return out.cpu().to(torch.float64).numpy()
 
 
-def _check(seed, lengths, nq, **kw):
+def _check(seed, lengths, nq, scale_sign=1.0, **kw):
     q, k, v, t, lens, qs, bs = _case(seed, lengths, nq, **kw)
-    scale = 1.0 / np.sqrt(q.shape[2])
+    return _compare(q, k, v, t, lens, qs, bs, scale_sign / np.sqrt(q.shape[2]))
+
+
+def _compare(q, k, v, t, lens, qs, bs, scale):
     got = _run(q, k, v, t, lens, qs, bs, scale)
     want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "bf16")
     assert got.shape == want.shape
@@ -157,3 +160,31 @@ def test_rejects_f32_pools_and_bad_arguments():
         pa.pa_prefill(qb, kb, kb, tab, lens, qs.long(), 16, 1.0, torch.empty_like(qb))
     with pytest.raises(ValueError):
         pa.pa_prefill(qb, kb, kb, tab, lens, qs[:1], 16, 1.0, torch.empty_like(qb))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_two_row_block_path(D):
+    """Full prefill of eight prompts of 199-256 tokens at the Llama-3-8B head
+    layout (32 query / 8 KV heads): enough query blocks (560 workgroups) for
+    the kernel to take two 16-row blocks per wave."""
+    lengths = [256, 250, 256, 241, 256, 256, 199, 256]
+    _check(31 + D, lengths, lengths, G=4, H_kv=8, D=D)
+
+
+def test_negative_scale():
+    """scale < 0 is applied exactly (the kernel negates the query instead)."""
+    _check(41, [77, 300], [77, 150], scale_sign=-1.0)
+
+
+def test_rising_logits_rescale_inside_the_key_loop():
+    """Logits that rise along the keys (key p scaled by 0.05 p against a
+    constant query) overtake the softmax reference about every 2.5 tiles, so
+    the rescale runs at tiles of both parities of the key loop."""
+    lengths, nq = [700, 333], [300, 333]
+    q, k, v, t, lens, qs, bs = _case(77, lengths, nq, G=4, H_kv=2, D=128)
+    q[:] = W.round_to_bf16_bits(np.full(q.shape, 0.125, np.float32))
+    for b, L in enumerate(lengths):
+        for p in range(L):
+            k[t[b, p // bs], :, p % bs] = W.round_to_bf16_bits(np.full((2, 128), 0.05 * p, np.float32))
+    _compare(q, k, v, t, lens, qs, bs, 1.0 / np.sqrt(128))
+
