@@ -199,46 +199,51 @@ prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- K/V tile gather: thread tid moves pieces tid + 256 h (row
-  // piece / kPPR, 16-byte column piece % kPPR) of each matrix.
+  // ---- K/V tile gather: thread tid moves row tid / 8 of every tile, its
+  // kLoads 16-byte column pieces from (tid % 8) * kLoads on, of K and of V:
+  // one table entry and one address per tile.  Pool rows are numbered in
+  // 32 bits (the host bounds num_blocks * H_kv * bs).
   const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
+  const int my_row = tid >> 3, col0 = (tid & 7) * kLoads;
   const int32_t bs_mask = (1 << log2_bs) - 1;
-  const char* kbase = reinterpret_cast<const char*>(a.pool.k_cache);
-  const char* vbase = reinterpret_cast<const char*>(a.pool.v_cache);
-  auto table_entries = [&](int32_t kt, int32_t (&tb)[kLoads]) {
+  const int32_t rows_per_block = H_kv << log2_bs, kv_row = kvh << log2_bs;
+  const char* kbase = reinterpret_cast<const char*>(a.pool.k_cache) + col0 * 16;
+  const char* vbase = reinterpret_cast<const char*>(a.pool.v_cache) + col0 * 16;
+  const int32_t nb1 = a.pool.num_blocks - 1;
+  auto table_entry = [&](int32_t kt) -> int32_t {
+    const int32_t key = min(kt * kKT + my_row, L - 1);
+    return trow[min(key >> log2_bs, a.max_blocks - 1)];
+  };
+  // Every lane loads (the row is clamped into the cache), so the number of
+  // loads in flight is the same on every path; stash zeroes rows past it.
+  auto gather = [&](int32_t kt, int32_t tb, u32x4_t (&kr)[kLoads], u32x4_t (&vr)[kLoads]) {
+    const int32_t key = min(kt * kKT + my_row, L - 1);
+    const uint32_t row = (uint32_t)(min(max(tb, 0), nb1) * rows_per_block + kv_row) +
+                         (uint32_t)(key & bs_mask);
+    const uint64_t off = (uint64_t)row * Geo::kRowBytes;
 #pragma unroll
     for (int h = 0; h < kLoads; ++h) {
-      const int32_t key = min(kt * kKT + (tid + h * kThreads) / Geo::kPPR, L - 1);
-      tb[h] = trow[min(key >> log2_bs, a.max_blocks - 1)];
+      kr[h] = *reinterpret_cast<const u32x4_t*>(kbase + off + h * 16);
+      vr[h] = *reinterpret_cast<const u32x4_t*>(vbase + off + h * 16);
     }
   };
-  auto gather = [&](int32_t kt, const int32_t (&tb)[kLoads], u32x4_t (&kr)[kLoads],
-                    u32x4_t (&vr)[kLoads]) {
-#pragma unroll
-    for (int h = 0; h < kLoads; ++h) {
-      const int p = tid + h * kThreads;
-      const int32_t key = kt * kKT + p / Geo::kPPR;
-      const int32_t phys = min(max(tb[h], 0), a.pool.num_blocks - 1);
-      const int64_t off =
-          ((((int64_t)phys * H_kv + kvh) << log2_bs) + (min(key, L - 1) & bs_mask)) *
-              Geo::kRowBytes + (p % Geo::kPPR) * 16;
-      // Every lane loads (the row is clamped into the cache), so the number
-      // of loads in flight is the same on every path; stash zeroes the rows
-      // past the cache.
-      kr[h] = *reinterpret_cast<const u32x4_t*>(kbase + off);
-      vr[h] = *reinterpret_cast<const u32x4_t*>(vbase + off);
-    }
-  };
+  const int lds_off = my_row * Geo::kRowLds + col0 * 16;
   auto stash = [&](int32_t kt, int stage, const u32x4_t (&kr)[kLoads],
                    const u32x4_t (&vr)[kLoads]) {
-    char* kt_l = tiles + stage * Geo::kStage;
+    char* kl = tiles + stage * Geo::kStage + lds_off;
+    if (kt * kKT + kKT > L) {  // uniform: the tile reaches past the cache
+      const bool in = kt * kKT + my_row < L;
 #pragma unroll
-    for (int h = 0; h < kLoads; ++h) {
-      const int p = tid + h * kThreads;
-      const int o = (p / Geo::kPPR) * Geo::kRowLds + (p % Geo::kPPR) * 16;
-      const bool in = kt * kKT + p / Geo::kPPR < L;  // rows past the cache are zeros
-      *reinterpret_cast<u32x4_t*>(kt_l + o) = in ? kr[h] : u32x4_t{0, 0, 0, 0};
-      *reinterpret_cast<u32x4_t*>(kt_l + Geo::kMat + o) = in ? vr[h] : u32x4_t{0, 0, 0, 0};
+      for (int h = 0; h < kLoads; ++h) {
+        *reinterpret_cast<u32x4_t*>(kl + h * 16) = in ? kr[h] : u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<u32x4_t*>(kl + Geo::kMat + h * 16) = in ? vr[h] : u32x4_t{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < kLoads; ++h) {
+        *reinterpret_cast<u32x4_t*>(kl + h * 16) = kr[h];
+        *reinterpret_cast<u32x4_t*>(kl + Geo::kMat + h * 16) = vr[h];
+      }
     }
   };
 
@@ -264,22 +269,48 @@ prefill_kernel(PrefillArgs a) {
 
   // Raw scores of a tile: s[kb][r], lane 16j + c, register q = key
   // t0 + 16 kb + 4j + q against row c of block r; masked keys are -inf.
+  // front also reads the tile's V words (vw) right after the QK MFMAs, so
+  // their LDS latency overlaps the softmax.
   floatx4_t s[2][R];
+  uint32_t vw[2][4][kBlk / 2];  // V rows 16 kb + 4j + q, columns kBlk*c ..
   auto front = [&](int stage, int32_t t0, bool masked) -> bool {
     const char* Kl = tiles + stage * Geo::kStage;
+    const char* Vl = Kl + Geo::kMat;
+    u32x4_t kf[2][kDS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ds = 0; ds < kDS; ++ds)
+        kf[kb][ds] = *reinterpret_cast<const u32x4_t*>(
+            Kl + (kb * 16 + c16) * Geo::kRowLds + ds * 64 + jr * 16);
+    __builtin_amdgcn_sched_barrier(0);  // all K reads in flight before the first MFMA
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < R; ++r) s[kb][r] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ds = 0; ds < kDS; ++ds) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(
-            Kl + (kb * 16 + c16) * Geo::kRowLds + ds * 64 + jr * 16);
 #pragma unroll
         for (int r = 0; r < R; ++r)
           s[kb][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, kf), __builtin_bit_cast(bf16x8_t, qf[r][ds]),
+              __builtin_bit_cast(bf16x8_t, kf[kb][ds]), __builtin_bit_cast(bf16x8_t, qf[r][ds]),
               s[kb][r], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const char* vp = Vl + (kb * 16 + 4 * jr + q) * Geo::kRowLds + c16 * (kBlk * 2);
+        if constexpr (kBlk == 8) {
+          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) vw[kb][q][w] = x[w];
+        } else {
+          const uint2 x = *reinterpret_cast<const uint2*>(vp);
+          vw[kb][q][0] = x.x;
+          vw[kb][q][1] = x.y;
+        }
       }
     }
     if (masked) {
@@ -291,13 +322,14 @@ prefill_kernel(PrefillArgs a) {
           for (int q = 0; q < 4; ++q)
             if (t0 + kb * 16 + 4 * jr + q > lim[r]) s[kb][r][q] = -INFINITY;
     }
+    // Any score above its row's threshold: plain compares (no reduction).
     bool hi = false;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float m = fmaxf(fmaxf(fmaxf(s[0][r][0], s[0][r][1]), fmaxf(s[0][r][2], s[0][r][3])),
-                            fmaxf(fmaxf(s[1][r][0], s[1][r][1]), fmaxf(s[1][r][2], s[1][r][3])));
-      hi = hi || m > thr[r];
-    }
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hi |= s[kb][r][q] > thr[r];
     return __ballot(hi) != 0;
   };
   // Raises the references to the tile's row maxima (where larger) and
@@ -323,8 +355,7 @@ prefill_kernel(PrefillArgs a) {
   };
   // p = 2^(score * scale - ref) as the 32-deep operand (the lane's keys
   // 4j..4j+3, then 16+4j..16+4j+3), l += P 1, O += P V.
-  auto back = [&](int stage) {
-    const char* Vl = tiles + stage * Geo::kStage + Geo::kMat;
+  auto back = [&]() {
     u32x4_t pp[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -340,24 +371,6 @@ prefill_kernel(PrefillArgs a) {
       }
       l[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pp[r]), ones,
                                                      l[r], 0, 0, 0);
-    }
-    // V rows 4j + q and 16 + 4j + q, columns kBlk * c .. kBlk * c + kBlk - 1.
-    uint32_t vw[2][4][kBlk / 2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const char* vp = Vl + (kb * 16 + 4 * jr + q) * Geo::kRowLds + c16 * (kBlk * 2);
-        if constexpr (kBlk == 8) {
-          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) vw[kb][q][w] = x[w];
-        } else {
-          const uint2 x = *reinterpret_cast<const uint2*>(vp);
-          vw[kb][q][0] = x.x;
-          vw[kb][q][1] = x.y;
-        }
-      }
     }
     // For column group blk the lane's operand is V[key][kBlk*c+blk] over
     // its 8 keys, in P's key order.
@@ -385,26 +398,26 @@ prefill_kernel(PrefillArgs a) {
   // order).  A tile whose logits exceed a reference leaves the inner loop
   // (after its one barrier, like every tile) to be rescaled and finished
   // outside it, so the hot loop touches the accumulators only through MFMA.
-  int32_t tb[2][kLoads];
+  int32_t tb[2];
   u32x4_t kr[2][kLoads], vr[2][kLoads];
   // Tiles past the last are gathered too (clamped, never used): the loads
   // are unconditional so that the waits stay exact.
-  table_entries(0, tb[0]);
-  table_entries(1, tb[1]);
+  tb[0] = table_entry(0);
+  tb[1] = table_entry(1);
   gather(0, tb[0], kr[0], vr[0]);
-  table_entries(2, tb[0]);
+  tb[0] = table_entry(2);
   gather(1, tb[1], kr[1], vr[1]);
   // One tile: returns true when it must be rescaled (its scores in s).
   auto step = [&](int32_t kt, auto kSet) -> bool {
     constexpr int x = decltype(kSet)::value, y = 1 - x;
     stash(kt, x, kr[x], vr[x]);
-    table_entries(kt + 3, tb[y]);
+    tb[y] = table_entry(kt + 3);
     gather(kt + 2, tb[x], kr[x], vr[x]);
     pa::lds_barrier();
     const int32_t t0 = kt * kKT;
     if (wave_live && t0 <= wp_max) {
       if (front(x, t0, t0 + kKT - 1 > wp_min)) return true;
-      back(x);
+      back();
     }
     return false;
   };
@@ -437,7 +450,7 @@ prefill_kernel(PrefillArgs a) {
     }
     if (brk < 0) break;
     rescale();
-    back(brk);
+    back();
     ++kt;
   }
 
@@ -533,6 +546,8 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
   if ((int64_t)max_blocks_per_seq * block_size > INT32_MAX)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq * block_size overflows int32");
   if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if ((int64_t)desc->num_blocks * desc->num_kv_heads * block_size > INT32_MAX)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: pool of more than 2^31 rows per pool");
   if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");

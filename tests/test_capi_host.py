@@ -105,6 +105,10 @@ def test_prefill_validates_on_the_host():
     assert call(q=None) == pa.PA_ERR_INVALID_ARGUMENT and b"NULL" in lib.pa_last_error()
     assert call(out=p8) == pa.PA_ERR_INVALID_ARGUMENT and b"misaligned" in lib.pa_last_error()
     assert call(tables=ctypes.c_void_p((1 << 20) + 2)) == pa.PA_ERR_INVALID_ARGUMENT
+    big = pa.CacheDesc(1 << 24, 16, 8, 128, pa.PA_BF16)  # 2^31 pool rows
+    st_ = lib.pa_prefill(p16, p16, p16, p16, 4, p16, p16, 2, 4, 16, 1.0, p16, 32,
+                         ctypes.byref(big), None)
+    assert st_ == pa.PA_ERR_UNSUPPORTED and b"2^31" in lib.pa_last_error()
     wide = pa.CacheDesc(16, 16, 1 << 16, 128, pa.PA_BF16)  # 65,536 KV heads, group 1
     st_ = lib.pa_prefill(p16, p16, p16, p16, 4, p16, p16, 8192, 2**31 - 1, 16, 1.0, p16, 1 << 16,
                          ctypes.byref(wide), None)
