@@ -77,9 +77,10 @@ struct PrefillArgs {
 template <int D>
 struct TileGeo {
   static constexpr int kRowBytes = D * 2;
-  // LDS rows padded to 1.5x: the fastest of the paddings measured (bank
-  // conflict cycles fall to a half of the 16-byte padding's).
-  static constexpr int kRowLds = kRowBytes + kRowBytes / 2;
+  // LDS rows padded by 32 bytes: of the paddings measured (16, 32, 64
+  // bytes, 1.5x) the one with the fewest bank-conflict cycles (with 64)
+  // and the least LDS.
+  static constexpr int kRowLds = kRowBytes + 32;
   static constexpr int kMat = kKT * kRowLds;           // one K or V tile in LDS
   static constexpr int kStage = 2 * kMat;              // K then V
   static constexpr int kPPR = kRowBytes / 16;          // 16-byte pieces per row
@@ -200,11 +201,13 @@ prefill_kernel(PrefillArgs a) {
   }
 
   // ---- K/V tile gather: thread tid moves row tid / 8 of every tile, its
-  // kLoads 16-byte column pieces from (tid % 8) * kLoads on, of K and of V:
-  // one table entry and one address per tile.  Pool rows are numbered in
-  // 32 bits (the host bounds num_blocks * H_kv * bs).
+  // 16-byte column pieces (tid % 8) + 8 h (h < kLoads), of K and of V: one
+  // table entry and one address per tile, and 8 lanes store 128
+  // contiguous bytes of a row at a time.  Pool rows are numbered in 32 bits
+  // (the host bounds num_blocks * H_kv * bs).
   const int32_t* trow = a.tables + (int64_t)b * a.max_blocks;
-  const int my_row = tid >> 3, col0 = (tid & 7) * kLoads;
+  const int my_row = tid >> 3, col0 = tid & 7;
+  constexpr int kPieceStep = 8 * 16;
   const int32_t bs_mask = (1 << log2_bs) - 1;
   const int32_t rows_per_block = H_kv << log2_bs, kv_row = kvh << log2_bs;
   const char* kbase = reinterpret_cast<const char*>(a.pool.k_cache) + col0 * 16;
@@ -223,8 +226,8 @@ prefill_kernel(PrefillArgs a) {
     const uint64_t off = (uint64_t)row * Geo::kRowBytes;
 #pragma unroll
     for (int h = 0; h < kLoads; ++h) {
-      kr[h] = *reinterpret_cast<const u32x4_t*>(kbase + off + h * 16);
-      vr[h] = *reinterpret_cast<const u32x4_t*>(vbase + off + h * 16);
+      kr[h] = *reinterpret_cast<const u32x4_t*>(kbase + off + h * kPieceStep);
+      vr[h] = *reinterpret_cast<const u32x4_t*>(vbase + off + h * kPieceStep);
     }
   };
   const int lds_off = my_row * Geo::kRowLds + col0 * 16;
@@ -235,14 +238,14 @@ prefill_kernel(PrefillArgs a) {
       const bool in = kt * kKT + my_row < L;
 #pragma unroll
       for (int h = 0; h < kLoads; ++h) {
-        *reinterpret_cast<u32x4_t*>(kl + h * 16) = in ? kr[h] : u32x4_t{0, 0, 0, 0};
-        *reinterpret_cast<u32x4_t*>(kl + Geo::kMat + h * 16) = in ? vr[h] : u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<u32x4_t*>(kl + h * kPieceStep) = in ? kr[h] : u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<u32x4_t*>(kl + Geo::kMat + h * kPieceStep) = in ? vr[h] : u32x4_t{0, 0, 0, 0};
       }
     } else {
 #pragma unroll
       for (int h = 0; h < kLoads; ++h) {
-        *reinterpret_cast<u32x4_t*>(kl + h * 16) = kr[h];
-        *reinterpret_cast<u32x4_t*>(kl + Geo::kMat + h * 16) = vr[h];
+        *reinterpret_cast<u32x4_t*>(kl + h * kPieceStep) = kr[h];
+        *reinterpret_cast<u32x4_t*>(kl + Geo::kMat + h * kPieceStep) = vr[h];
       }
     }
   };
