@@ -42,6 +42,29 @@ Readings adopted where the pages are silent (stated once, used everywhere):
 * A call that runs out of blocks changes nothing (all-or-nothing over the
   whole call) and raises ``OutOfBlocks``; the policy for that case belongs
   to the caller [P1, FAQ "What happens when the GPU runs out of KV blocks?"].
+
+Preemption by swapping [P1, Common questions, "What happens when the GPU runs
+out of KV blocks?": the runtime may move blocks to CPU memory, or drop them
+and recompute from the tokens; P3, Follow-up questions, "What happens when
+the GPU runs out of free blocks?": a preempted request's blocks are swapped to
+CPU memory or dropped and recomputed later in one prefill pass].  Readings:
+
+* An optional second pool of host (CPU memory) blocks with its own LIFO free
+  stack (``add_host_pool``), handed out in ``free_order`` like the device
+  pool.
+* ``swap_out`` moves a whole sequence: one host block per logical block, in
+  logical order, with a (device block, host block) pair per block for the
+  caller's copy; then the device blocks are released exactly as by a free
+  (reverse logical order, pushed when their count reaches zero).  A block
+  the sequence shares with others is copied and stays on the device for
+  them.
+* ``swap_in`` is the reverse: one fresh device block per logical block (count
+  1), a (host block, device block) pair each, then the host blocks return to
+  the host stack in reverse logical order.  Sharing is not restored.
+* Both are all-or-nothing (``OutOfBlocks`` when the target pool is short).
+  A swapped-out sequence cannot reserve, fork or build a table; freeing it
+  returns its host blocks.  The drop-and-recompute path needs no new state:
+  free the sequence, create it again, reserve its tokens and prefill.
 """
 
 from __future__ import annotations
@@ -83,6 +106,8 @@ class BlockAllocator:
         self._rc = [0] * num_blocks
         self._table: dict[int, list[int]] = {}
         self._ntok: dict[int, int] = {}
+        self._host_free: list[int] | None = None  # host stack, top at the end
+        self._swapped: set[int] = set()
 
     # ------------------------------------------------------------------ state
     def num_free(self) -> int:
@@ -108,6 +133,68 @@ class BlockAllocator:
     def seq_ids(self) -> list[int]:
         return sorted(self._table)
 
+    def num_free_host(self) -> int:
+        return -1 if self._host_free is None else len(self._host_free)
+
+    def host_free_list(self) -> list[int]:
+        if self._host_free is None:
+            raise InvalidArgument("no host pool")
+        return list(reversed(self._host_free))
+
+    def seq_is_swapped(self, seq_id: int) -> bool:
+        self._need(seq_id)
+        return seq_id in self._swapped
+
+    # ------------------------------------------------------------ host pool
+    def add_host_pool(self, num_host_blocks: int, free_order=None) -> None:
+        if self._host_free is not None:
+            raise InvalidArgument("host pool exists")
+        if num_host_blocks < 1:
+            raise InvalidArgument("num_host_blocks must be >= 1")
+        order = (list(range(num_host_blocks)) if free_order is None
+                 else [int(x) for x in free_order])
+        if sorted(order) != list(range(num_host_blocks)):
+            raise InvalidArgument("free_order must be a permutation")
+        self._host_free = list(reversed(order))
+
+    def swap_out(self, seq_id: int):
+        """Move the sequence to host blocks; returns (device, host) pairs."""
+        self._need(seq_id)
+        if seq_id in self._swapped:
+            raise InvalidArgument("sequence is swapped out")
+        if self._host_free is None:
+            raise InvalidArgument("no host pool")
+        table = self._table[seq_id]
+        if len(table) > len(self._host_free):
+            raise OutOfBlocks("no free host block")
+        host = [self._host_free.pop() for _ in table]
+        pairs = list(zip(table, host))
+        for blk in reversed(table):
+            self._rc[blk] -= 1
+            if self._rc[blk] == 0:
+                self._free.append(blk)
+        self._table[seq_id] = host
+        self._swapped.add(seq_id)
+        return pairs
+
+    def swap_in(self, seq_id: int):
+        """Move a swapped-out sequence back; returns (host, device) pairs."""
+        self._need(seq_id)
+        if seq_id not in self._swapped:
+            raise InvalidArgument("sequence is not swapped out")
+        host = self._table[seq_id]
+        if len(host) > len(self._free):
+            raise OutOfBlocks("no free block")
+        dev = [self._free.pop() for _ in host]
+        for blk in dev:
+            self._rc[blk] = 1
+        pairs = list(zip(host, dev))
+        for blk in reversed(host):
+            self._host_free.append(blk)
+        self._table[seq_id] = dev
+        self._swapped.discard(seq_id)
+        return pairs
+
     # -------------------------------------------------------------- sequences
     def seq_create(self, seq_id: int) -> None:
         if seq_id in self._table:
@@ -118,6 +205,8 @@ class BlockAllocator:
     def seq_fork(self, parent: int, child: int) -> None:
         """Child shares every physical block of the parent (count + 1 each)."""
         self._need(parent)
+        if parent in self._swapped:
+            raise InvalidArgument("sequence is swapped out")
         if child in self._table:
             raise InvalidArgument("child exists")
         self._table[child] = list(self._table[parent])
@@ -128,10 +217,14 @@ class BlockAllocator:
     def seq_free(self, seq_id: int) -> None:
         """Drop one reference to each block; zero-count blocks rejoin the pool."""
         self._need(seq_id)
-        for blk in reversed(self._table[seq_id]):
-            self._rc[blk] -= 1
-            if self._rc[blk] == 0:
-                self._free.append(blk)
+        if seq_id in self._swapped:
+            self._host_free.extend(reversed(self._table[seq_id]))
+            self._swapped.discard(seq_id)
+        else:
+            for blk in reversed(self._table[seq_id]):
+                self._rc[blk] -= 1
+                if self._rc[blk] == 0:
+                    self._free.append(blk)
         del self._table[seq_id]
         del self._ntok[seq_id]
 
@@ -152,6 +245,8 @@ class BlockAllocator:
                 raise InvalidArgument("negative token count")
             if sid not in self._table:
                 raise UnknownSeq(f"unknown sequence {sid}")
+            if sid in self._swapped:
+                raise InvalidArgument("sequence is swapped out")
             if sid in seen:
                 raise InvalidArgument("sequence listed twice")
             seen.add(sid)
@@ -173,6 +268,8 @@ class BlockAllocator:
         for sid in seq_ids:
             sid = int(sid)
             self._need(sid)
+            if sid in self._swapped:
+                raise InvalidArgument("sequence is swapped out")
             tab = self._table[sid]
             if len(tab) > max_blocks:
                 raise InvalidArgument("table longer than max_blocks")

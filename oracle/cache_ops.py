@@ -53,3 +53,19 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs):
     for s, d in pairs.tolist():
         k_cache[d] = k_cache[s]
         v_cache[d] = v_cache[s]
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs):
+    """Copy whole blocks from one pool pair to another: ``dst[d] = src[s]``.
+
+    A preempted sequence's blocks move to CPU memory and back ["What is
+    paged attention in vLLM...", Follow-up questions, "What happens when the
+    GPU runs out of free blocks?": blocks are swapped to CPU memory or
+    dropped and recomputed; "Paged Attention" glossary, Common questions,
+    "What happens when the GPU runs out of KV blocks?"].  The two pools have the same
+    block geometry and may differ in block count.
+    """
+    pairs = np.asarray(src_dst_pairs, dtype=np.int64).reshape(-1, 2)
+    for s, d in pairs.tolist():
+        dst_k[d] = src_k[s]
+        dst_v[d] = src_v[s]
