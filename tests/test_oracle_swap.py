@@ -221,10 +221,13 @@ class _HostFifo(BlockAllocator):
     """Host blocks taken from the bottom of the host stack."""
 
     def swap_out(self, seq_id):
+        if self._host_free is None:
+            return super().swap_out(seq_id)
         self._host_free.reverse()
-        pairs = super().swap_out(seq_id)
-        self._host_free.reverse()
-        return pairs
+        try:
+            return super().swap_out(seq_id)
+        finally:
+            self._host_free.reverse()
 
 
 class _SwapInPartial(BlockAllocator):
