@@ -67,7 +67,8 @@ def parse():
                    help="llama3_8b_decode (the default bench line), or serving_batch, "
                         "block_size_sweep_bs{8,16,32,128}, prefix_sharing_p{2056,2048}: pa_decode "
                         "alone on that workload's batch (kernel leg only); llama3_8b_prefill, "
-                        "llama3_8b_chunked_prefill_cN: pa_prefill alone on the worked batch")
+                        "llama3_8b_chunked_prefill_cN: pa_prefill alone on the worked batch; "
+                        "swap_llama3_8b: pa_swap_blocks out to pinned host memory and back")
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying a captured HIP graph")
     return p.parse_args()
@@ -373,6 +374,68 @@ def cpu_baseline_prefill(seed, chunk, seconds):
                       f"{el:.1f} s, NumPy fp64 paged prefill incl. bf16 widening"}
 
 
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, per direction
+
+
+def swap_workload(args):
+    """pa_swap_blocks alone: every block of the worked Llama-3-8B batch (665
+    blocks of 64 KiB, all eight sequences preempted) from the device pool to
+    a pinned host pool, and back into other device blocks, as the C
+    allocator's swap-out and swap-in emit the pairs.  One launch per
+    direction, captured in a graph and replayed args.kernel_reps times."""
+    import torch
+
+    import paged_kv_cache_338_amd as pa
+    import workloads as W
+
+    dev = "cuda:0"
+    w = W.llama3_8b_decode(with_values=False)
+    alloc = pa.Allocator(w.num_blocks, w.block_size, w.free_order)
+    for op in w.script:
+        if op[0] == "create":
+            alloc.seq_create(op[1])
+        else:
+            alloc.seq_reserve(op[1], op[2], cow_cap=len(op[1]))
+    nblk = sum(len(alloc.seq_block_table(s)) for s in w.seq_ids)
+    alloc.add_host_pool(nblk, np.random.default_rng(w.seed).permutation(nblk))
+    out_pairs = np.concatenate([alloc.seq_swap_out(s) for s in w.seq_ids])
+    in_pairs = np.concatenate([alloc.seq_swap_in(s) for s in w.seq_ids])
+    shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+    hshape = (nblk,) + shape[1:]
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    kp = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    vp = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    hk = torch.empty(hshape, dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty(hshape, dtype=torch.bfloat16).pin_memory()
+    po = torch.from_numpy(out_pairs).to(dev)
+    pi = torch.from_numpy(in_pairs).to(dev)
+    block_bytes = 2 * w.num_kv_heads * w.block_size * w.head_dim * 2  # K and V, bf16
+    moved = nblk * block_bytes
+    us_out = replay_timed(lambda: [pa.prepare_swap_blocks(po, nblk, kp, vp, hk, hv)],
+                          args.kernel_reps)
+    us_in = replay_timed(lambda: [pa.prepare_swap_blocks(pi, nblk, hk, hv, kp, vp)],
+                         args.kernel_reps)
+    gbs_out, gbs_in = moved / (us_out * 1e-6) / 1e9, moved / (us_in * 1e-6) / 1e9
+    both = 2 * moved / ((us_out + us_in) * 1e-6) / 1e9
+    log(f"swap: {nblk} blocks, {moved} B each way: out {us_out:.1f} us ({gbs_out:.1f} GB/s), "
+        f"in {us_in:.1f} us ({gbs_in:.1f} GB/s)")
+    print(json.dumps({
+        "metric": "preemption swap GB/s (device pool <-> pinned host pool), Llama-3-8B batch",
+        "value": round(both, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.kernel_reps,
+        "warmup": 1, "ms_per_step": round((us_out + us_in) / 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap_llama3_8b: all 8 sequences of the worked batch swapped out "
+                               "to pinned host blocks and back in to other device blocks, one "
+                               "pa_swap_blocks launch per direction, graph replay",
+                   "blocks": int(nblk), "bytes_each_way": int(moved),
+                   "us_swap_out": round(us_out, 2), "us_swap_in": round(us_in, 2),
+                   "gbs_swap_out": round(gbs_out, 2), "gbs_swap_in": round(gbs_in, 2)},
+        "roofline": {"bound": "host-link", "achieved": round(both, 2), "peak": HOST_LINK_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(both / HOST_LINK_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "pa_swap_blocks (move_blocks_kernel), one "
+                                                "launch per direction"}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -385,6 +448,8 @@ def main():
             args.layers = 2  # each of these batches is larger than the last-level cache
         if "prefill" in args.workload:
             prefill_workload(args)
+        elif args.workload == "swap_llama3_8b":
+            swap_workload(args)
         else:
             other_workload(args)
         return

@@ -119,6 +119,29 @@ pa_status pa_cache_append(const void* k, const void* v, const int64_t* slot_mapp
 pa_status pa_copy_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, void* k_cache,
                          void* v_cache, const pa_cache_desc* desc, void* stream);
 
+/* Whole-block moves between two pool pairs of one geometry, for preemption
+ * by swapping [P1 Common questions, "What happens when the GPU runs out of
+ * KV blocks?": blocks may move to CPU memory; P3 Follow-up questions, "What
+ * happens when the GPU runs out of free blocks?": a preempted request's
+ * blocks are swapped to CPU memory, or dropped and recomputed].
+ *
+ * For every pair i < num_pairs: block dst = src_dst_pairs[2i+1] of dst_k and
+ * dst_v becomes a bit copy of block src = src_dst_pairs[2i] of src_k and
+ * src_v (all heads, all slots).  The pairs come from pa_seq_swap_out
+ * (device pool -> host pool) or pa_seq_swap_in (host pool -> device pool).
+ * src_k/src_v:  [src_num_blocks][H_kv][bs][D], dst_k/dst_v:
+ *   [dst_num_blocks][H_kv][bs][D]; block_size, num_kv_heads, head_dim and
+ *   dtype come from desc (its num_blocks is not used).  Either pair may be
+ *   pinned host memory the GPU can address (hipHostMalloc, torch
+ *   pin_memory=True); the other is device memory.
+ * src_dst_pairs: int32 [num_pairs][2], device memory or pinned host memory.
+ *   Destinations must be distinct; ids outside a pool are skipped.
+ * Asynchronous on stream; num_pairs == 0 enqueues nothing.  The caller
+ * orders it before any reuse of the source blocks (stream order). */
+pa_status pa_swap_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, const void* src_k,
+                         const void* src_v, int32_t src_num_blocks, void* dst_k, void* dst_v,
+                         int32_t dst_num_blocks, const pa_cache_desc* desc, void* stream);
+
 /* Single-query (decode) attention through the block tables [P1 body: the
  * kernel derives each token's logical block and offset, looks up the
  * physical block and reads K/V there without first gathering the sequence;
@@ -205,6 +228,13 @@ pa_status pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
  *   call order, so the last remaining sharer writes in place.  A full shared
  *   block is never copied (the next token takes a fresh block).
  * - Every call gives the strong guarantee: on any error nothing changed.
+ * - Preemption [P1 Common questions and P3 Follow-up questions, on running
+ *   out of blocks]: an optional pool of host blocks with its own LIFO stack.
+ *   Swap-out moves a whole sequence to host blocks and releases its device
+ *   blocks as a free does (shared blocks stay with the other sharers);
+ *   swap-in moves it back into private device blocks.  Drop-and-recompute
+ *   needs no new call: pa_seq_free, pa_seq_create, pa_seq_reserve, then
+ *   append and prefill.
  * Handles are owned by the caller (create/destroy); not thread-safe. */
 typedef struct pa_allocator pa_allocator;
 
@@ -251,6 +281,42 @@ pa_status pa_block_refcount(const pa_allocator* alloc, int32_t block, int32_t* o
 pa_status pa_seq_block_table(const pa_allocator* alloc, int64_t seq_id, int32_t* out,
                              int32_t cap, int32_t* len);
 pa_status pa_seq_num_tokens(const pa_allocator* alloc, int64_t seq_id, int32_t* out);
+
+/* Adds the host block pool: num_host_blocks blocks handed out in free_order
+ * (host, a permutation of 0..num_host_blocks-1; NULL = ascending).
+ * INVALID_ARGUMENT if the allocator already has one. */
+pa_status pa_allocator_add_host_pool(pa_allocator* alloc, int32_t num_host_blocks,
+                                     const int32_t* free_order);
+
+/* Moves seq_id to host blocks: one host block per logical block, in logical
+ * order, popped from the host stack; pairs_out (host int32 [cap][2]) gets
+ * (device block, host block) per logical block for pa_swap_blocks; then the
+ * device blocks are released as by pa_seq_free (reverse logical order,
+ * pushed when their count reaches zero).  The sequence's table then holds
+ * host block ids; its length is unchanged.  Errors, in order: UNKNOWN_SEQ;
+ * INVALID_ARGUMENT if already swapped out or there is no host pool;
+ * OUT_OF_BLOCKS if the host pool is short; INVALID_ARGUMENT if cap is below
+ * the table length.  Each leaves the allocator unchanged. */
+pa_status pa_seq_swap_out(pa_allocator* alloc, int64_t seq_id, int32_t* pairs_out, int32_t cap,
+                          int32_t* num_pairs_out);
+
+/* Moves a swapped-out sequence back: one device block (count 1) per logical
+ * block from the device stack; pairs_out gets (host block, device block);
+ * then the host blocks return to the host stack in reverse logical order.
+ * Errors, in order: UNKNOWN_SEQ; INVALID_ARGUMENT if not swapped out;
+ * OUT_OF_BLOCKS if the device pool is short; INVALID_ARGUMENT if cap is too
+ * small.  A swapped-out sequence cannot be reserved, forked or put in a
+ * block table (INVALID_ARGUMENT); pa_seq_free returns its host blocks. */
+pa_status pa_seq_swap_in(pa_allocator* alloc, int64_t seq_id, int32_t* pairs_out, int32_t cap,
+                         int32_t* num_pairs_out);
+
+/* *out = 1 if seq_id is swapped out, else 0. */
+pa_status pa_seq_is_swapped(const pa_allocator* alloc, int64_t seq_id, int32_t* out);
+/* Free host blocks (-1 without a host pool), and the host stack, the block
+ * handed out next first (as pa_allocator_free_list). */
+int32_t pa_allocator_num_free_host(const pa_allocator* alloc);
+pa_status pa_allocator_host_free_list(const pa_allocator* alloc, int32_t* out, int32_t cap,
+                                      int32_t* len);
 
 #ifdef __cplusplus
 }

@@ -83,6 +83,13 @@ SIGNATURES = {
     "pa_block_refcount": (_I32, [_P, _I32, _PI32]),
     "pa_seq_block_table": (_I32, [_P, _I64, _PI32, _I32, _PI32]),
     "pa_seq_num_tokens": (_I32, [_P, _I64, _PI32]),
+    "pa_swap_blocks": (_I32, [_P, _I32, _P, _P, _I32, _P, _P, _I32, _PDESC, _P]),
+    "pa_allocator_add_host_pool": (_I32, [_P, _I32, _PI32]),
+    "pa_seq_swap_out": (_I32, [_P, _I64, _PI32, _I32, _PI32]),
+    "pa_seq_swap_in": (_I32, [_P, _I64, _PI32, _I32, _PI32]),
+    "pa_seq_is_swapped": (_I32, [_P, _I64, _PI32]),
+    "pa_allocator_num_free_host": (_I32, [_P]),
+    "pa_allocator_host_free_list": (_I32, [_P, _PI32, _I32, _PI32]),
 }
 
 _lib = None
@@ -143,6 +150,15 @@ def _dev(t, name):
     return t.data_ptr()
 
 
+def _addressable(t, name):
+    """A device tensor, or pinned host memory the GPU reads and writes."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -193,6 +209,32 @@ def pa_copy_blocks(src_dst_pairs, k_cache, v_cache, stream=None):
     _check(load_library().pa_copy_blocks(
         _dev(src_dst_pairs, "src_dst_pairs"), P, _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), ctypes.byref(desc), _stream(stream)))
+
+
+def pa_swap_blocks(src_dst_pairs, src_k, src_v, dst_k, dst_v, stream=None):
+    """Moves block src of (src_k, src_v) to block dst of (dst_k, dst_v) for each
+    row of int32 [P, 2]; either pool pair may be pinned host memory."""
+    prepare_swap_blocks(src_dst_pairs, src_dst_pairs.numel() // 2, src_k, src_v, dst_k, dst_v,
+                        stream)()
+
+
+def prepare_swap_blocks(src_dst_pairs, num_pairs, src_k, src_v, dst_k, dst_v, stream=None):
+    """pa_swap_blocks over the first num_pairs rows of a fixed pair buffer."""
+    torch = _torch()
+    _same_pool(src_k, src_v)
+    _same_pool(dst_k, dst_v)
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("source and destination pools differ in block geometry or dtype")
+    if src_dst_pairs.dtype != torch.int32 or src_dst_pairs.numel() < 2 * int(num_pairs):
+        raise ValueError("src_dst_pairs must be int32 [P, 2] with at least num_pairs rows")
+    desc = cache_desc(dst_k)
+    lib = load_library()
+    args = (_addressable(src_dst_pairs, "src_dst_pairs"), int(num_pairs),
+            _addressable(src_k, "src_k"), _addressable(src_v, "src_v"), src_k.shape[0],
+            _addressable(dst_k, "dst_k"), _addressable(dst_v, "dst_v"), dst_k.shape[0],
+            ctypes.byref(desc), _stream(stream))
+    return PreparedCall(lib.pa_swap_blocks, args, (src_dst_pairs, src_k, src_v, dst_k, dst_v,
+                                                   desc))
 
 
 def pa_decode_workspace_size(desc, num_seqs, num_q_heads, max_blocks_per_seq):
@@ -370,6 +412,50 @@ class Allocator:
         v = ctypes.c_int32(0)
         _check(self._lib.pa_seq_num_tokens(self._h, int(seq_id), ctypes.byref(v)))
         return v.value
+
+    # ---------------------------------------------------------- host pool
+    def add_host_pool(self, num_host_blocks, free_order=None):
+        if free_order is None:
+            _check(self._lib.pa_allocator_add_host_pool(self._h, int(num_host_blocks), None))
+        else:
+            fo = np.ascontiguousarray(free_order, dtype=np.int32)
+            if fo.size != int(num_host_blocks):
+                raise ValueError("free_order must have num_host_blocks entries")
+            _check(self._lib.pa_allocator_add_host_pool(self._h, int(num_host_blocks),
+                                                        _ptr(fo, ctypes.c_int32)))
+
+    def _swap(self, fn, seq_id):
+        ln = ctypes.c_int32(0)
+        self._lib.pa_seq_block_table(self._h, int(seq_id), None, 0, ctypes.byref(ln))
+        pairs = np.empty((max(ln.value, 1), 2), np.int32)
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, int(seq_id), _ptr(pairs, ctypes.c_int32), pairs.shape[0],
+                  ctypes.byref(n)))
+        return pairs[:n.value]
+
+    def seq_swap_out(self, seq_id):
+        """Returns int32 [n, 2] (device block, host block) pairs."""
+        return self._swap(self._lib.pa_seq_swap_out, seq_id)
+
+    def seq_swap_in(self, seq_id):
+        """Returns int32 [n, 2] (host block, device block) pairs."""
+        return self._swap(self._lib.pa_seq_swap_in, seq_id)
+
+    def seq_is_swapped(self, seq_id):
+        v = ctypes.c_int32(0)
+        _check(self._lib.pa_seq_is_swapped(self._h, int(seq_id), ctypes.byref(v)))
+        return bool(v.value)
+
+    def num_free_host(self):
+        return self._lib.pa_allocator_num_free_host(self._h)
+
+    def host_free_list(self):
+        n = self.num_free_host()
+        out = np.empty(max(n, 1), np.int32)
+        ln = ctypes.c_int32(0)
+        _check(self._lib.pa_allocator_host_free_list(self._h, _ptr(out, ctypes.c_int32), out.size,
+                                                     ctypes.byref(ln)))
+        return out[:ln.value].tolist()
 
 
 # ------------------------------------------------------- prepared launches

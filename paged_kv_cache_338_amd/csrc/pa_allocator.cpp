@@ -8,6 +8,15 @@
 // works, items 2, 4 and 5 (grow block by block; shared prefixes by reference
 // count; copy only the block being written).
 //
+// Preemption by swapping ("Paged Attention" glossary, Common questions, and
+// the clozo.ai page, Follow-up questions, on running out of blocks: a
+// preempted request's blocks move to CPU memory, or are dropped and
+// recomputed): an optional pool of host blocks with its own LIFO stack;
+// swap-out moves a whole sequence to host blocks in logical order and
+// releases its device blocks as a free does (shared blocks stay with the
+// other sharers); swap-in is the reverse, into private device blocks.  Both
+// check the target pool first, so they change nothing when it is short.
+//
 // Every entry point gives the strong guarantee: pa_seq_reserve keeps an undo
 // log while it walks the tokens and replays it backwards when it runs out of
 // blocks or out of room for copy pairs, so a failed call leaves the free
@@ -24,8 +33,9 @@
 namespace {
 
 struct Sequence {
-  std::vector<int32_t> table;  // logical block -> physical block
+  std::vector<int32_t> table;  // logical block -> physical block (host block when swapped)
   int32_t num_tokens = 0;
+  bool swapped = false;
 };
 
 // One reversible change made by a reserve call.
@@ -45,6 +55,9 @@ struct pa_allocator {
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, Sequence> seqs;
   std::vector<Undo> undo;  // reused between calls
+  bool has_host = false;
+  int32_t num_host_blocks = 0;
+  std::vector<int32_t> host_free;  // top at back()
 
   Sequence* find(int64_t id) {
     auto it = seqs.find(id);
@@ -131,6 +144,8 @@ pa_status pa_seq_fork(pa_allocator* alloc, int64_t parent, int64_t child) {
   if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
   const Sequence* p = alloc->find(parent);
   if (!p) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown parent sequence %lld", (long long)parent);
+  if (p->swapped)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is swapped out", (long long)parent);
   if (alloc->find(child))
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "child sequence %lld exists", (long long)child);
   Sequence copy = *p;  // copy before emplace: emplace may rehash
@@ -145,8 +160,12 @@ pa_status pa_seq_free(pa_allocator* alloc, int64_t seq_id) {
   if (it == alloc->seqs.end())
     return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
   const std::vector<int32_t>& t = it->second.table;
-  for (auto r = t.rbegin(); r != t.rend(); ++r) {
-    if (--alloc->refcount[*r] == 0) alloc->free_stack.push_back(*r);
+  if (it->second.swapped) {
+    for (auto r = t.rbegin(); r != t.rend(); ++r) alloc->host_free.push_back(*r);
+  } else {
+    for (auto r = t.rbegin(); r != t.rend(); ++r) {
+      if (--alloc->refcount[*r] == 0) alloc->free_stack.push_back(*r);
+    }
   }
   alloc->seqs.erase(it);
   return PA_OK;
@@ -173,6 +192,9 @@ pa_status pa_seq_reserve(pa_allocator* alloc, const int64_t* seq_ids, const int3
     seqs[i] = alloc->find(seq_ids[i]);
     if (!seqs[i])
       return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if (seqs[i]->swapped)
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is swapped out",
+                      (long long)seq_ids[i]);
     if (!seen.insert(seq_ids[i]).second)
       return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld listed twice",
                       (long long)seq_ids[i]);
@@ -247,6 +269,9 @@ pa_status pa_build_block_tables(const pa_allocator* alloc, const int64_t* seq_id
   for (int32_t i = 0; i < n; ++i) {
     const Sequence* s = alloc->find(seq_ids[i]);
     if (!s) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_ids[i]);
+    if (s->swapped)
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is swapped out",
+                      (long long)seq_ids[i]);
     if (static_cast<int64_t>(s->table.size()) > max_blocks_per_seq)
       return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld holds %zu blocks > %d",
                       (long long)seq_ids[i], s->table.size(), max_blocks_per_seq);
@@ -258,6 +283,113 @@ pa_status pa_build_block_tables(const pa_allocator* alloc, const int64_t* seq_id
     std::fill(row + s->table.size(), row + max_blocks_per_seq, -1);
     context_lens_out[i] = s->num_tokens;
   }
+  return PA_OK;
+}
+
+pa_status pa_allocator_add_host_pool(pa_allocator* alloc, int32_t num_host_blocks,
+                                     const int32_t* free_order) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  if (alloc->has_host) return pa::fail(PA_ERR_INVALID_ARGUMENT, "host pool exists");
+  if (num_host_blocks < 1)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_host_blocks (%d) must be >= 1", num_host_blocks);
+  if (free_order) {
+    std::vector<uint8_t> seen(num_host_blocks, 0);
+    for (int32_t i = 0; i < num_host_blocks; ++i) {
+      const int32_t x = free_order[i];
+      if (x < 0 || x >= num_host_blocks || seen[x])
+        return pa::fail(PA_ERR_INVALID_ARGUMENT,
+                        "free_order is not a permutation of 0..%d (entry %d = %d)",
+                        num_host_blocks - 1, i, x);
+      seen[x] = 1;
+    }
+  }
+  alloc->host_free.resize(num_host_blocks);
+  for (int32_t i = 0; i < num_host_blocks; ++i)
+    alloc->host_free[num_host_blocks - 1 - i] = free_order ? free_order[i] : i;
+  alloc->num_host_blocks = num_host_blocks;
+  alloc->has_host = true;
+  return PA_OK;
+}
+
+pa_status pa_seq_swap_out(pa_allocator* alloc, int64_t seq_id, int32_t* pairs_out, int32_t cap,
+                          int32_t* num_pairs_out) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  Sequence* s = alloc->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  if (s->swapped)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is swapped out", (long long)seq_id);
+  if (!alloc->has_host) return pa::fail(PA_ERR_INVALID_ARGUMENT, "no host pool");
+  const int32_t n = static_cast<int32_t>(s->table.size());
+  if (n > static_cast<int32_t>(alloc->host_free.size()))
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "no free host block (%zu free, %d needed)",
+                    alloc->host_free.size(), n);
+  if (cap < n) return pa::fail(PA_ERR_INVALID_ARGUMENT, "cap %d < %d pairs", cap, n);
+  if (n > 0 && !pairs_out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "pairs_out is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t h = alloc->host_free.back();
+    alloc->host_free.pop_back();
+    pairs_out[2 * i] = s->table[i];
+    pairs_out[2 * i + 1] = h;
+  }
+  for (int32_t i = n - 1; i >= 0; --i) {
+    const int32_t blk = s->table[i];
+    if (--alloc->refcount[blk] == 0) alloc->free_stack.push_back(blk);
+  }
+  for (int32_t i = 0; i < n; ++i) s->table[i] = pairs_out[2 * i + 1];
+  s->swapped = true;
+  if (num_pairs_out) *num_pairs_out = n;
+  return PA_OK;
+}
+
+pa_status pa_seq_swap_in(pa_allocator* alloc, int64_t seq_id, int32_t* pairs_out, int32_t cap,
+                         int32_t* num_pairs_out) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  Sequence* s = alloc->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  if (!s->swapped)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is not swapped out",
+                    (long long)seq_id);
+  const int32_t n = static_cast<int32_t>(s->table.size());
+  if (n > static_cast<int32_t>(alloc->free_stack.size()))
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "no free block (%zu free, %d needed)",
+                    alloc->free_stack.size(), n);
+  if (cap < n) return pa::fail(PA_ERR_INVALID_ARGUMENT, "cap %d < %d pairs", cap, n);
+  if (n > 0 && !pairs_out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "pairs_out is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t d = alloc->free_stack.back();
+    alloc->free_stack.pop_back();
+    alloc->refcount[d] = 1;
+    pairs_out[2 * i] = s->table[i];
+    pairs_out[2 * i + 1] = d;
+  }
+  for (int32_t i = n - 1; i >= 0; --i) alloc->host_free.push_back(s->table[i]);
+  for (int32_t i = 0; i < n; ++i) s->table[i] = pairs_out[2 * i + 1];
+  s->swapped = false;
+  if (num_pairs_out) *num_pairs_out = n;
+  return PA_OK;
+}
+
+pa_status pa_seq_is_swapped(const pa_allocator* alloc, int64_t seq_id, int32_t* out) {
+  if (!alloc || !out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL argument");
+  const Sequence* s = alloc->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  *out = s->swapped ? 1 : 0;
+  return PA_OK;
+}
+
+int32_t pa_allocator_num_free_host(const pa_allocator* alloc) {
+  return alloc && alloc->has_host ? static_cast<int32_t>(alloc->host_free.size()) : -1;
+}
+
+pa_status pa_allocator_host_free_list(const pa_allocator* alloc, int32_t* out, int32_t cap,
+                                      int32_t* len) {
+  if (!alloc || !len) return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (!alloc->has_host) return pa::fail(PA_ERR_INVALID_ARGUMENT, "no host pool");
+  const int32_t nf = static_cast<int32_t>(alloc->host_free.size());
+  *len = nf;
+  if (cap < nf) return pa::fail(PA_ERR_INVALID_ARGUMENT, "cap %d < %d free blocks", cap, nf);
+  if (nf > 0 && !out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "out is NULL");
+  std::copy(alloc->host_free.rbegin(), alloc->host_free.rend(), out);
   return PA_OK;
 }
 

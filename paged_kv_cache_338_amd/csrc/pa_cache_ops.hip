@@ -9,9 +9,17 @@
 // sequences is copied only when one of them writes into it, and only that
 // block is copied.
 //
-// Both kernels are pure data movement: 16-byte loads and stores, one
-// workgroup per token (append) or per (pair, pool) (copy).  Out-of-pool slots
-// and block ids are skipped, so a bad index never turns into a wild write.
+// Swap ("Paged Attention" glossary, Common questions, and the clozo.ai page,
+// Follow-up questions, on running out of blocks): a preempted sequence's
+// blocks move to CPU memory and back.  pa_swap_blocks moves whole blocks
+// between two pools of one geometry, either of which may be pinned host
+// memory the GPU reads and writes directly (one launch for any scattered
+// set of blocks; over the host link the transfer is bound by the link).
+//
+// All kernels are pure data movement: 16-byte loads and stores, one
+// workgroup per token (append) or per (pair, pool) (block moves).
+// Out-of-pool slots and block ids are skipped, so a bad index never turns
+// into a wild write.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -41,14 +49,16 @@ cache_append_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v,
   }
 }
 
+// Block src of the source pools -> block dst of the destination pools
+// (the same pools for a copy-on-write copy); blockIdx.y picks K or V.
 __global__ void __launch_bounds__(256)
-copy_blocks_kernel(const int32_t* __restrict__ pairs, uint4* __restrict__ k_cache,
-                   uint4* __restrict__ v_cache, int32_t num_blocks, int64_t block_vecs) {
+move_blocks_kernel(const int32_t* __restrict__ pairs, const uint4* src_k, const uint4* src_v,
+                   int32_t src_blocks, uint4* dst_k, uint4* dst_v, int32_t dst_blocks,
+                   int64_t block_vecs) {
   const int32_t src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  uint4* base = blockIdx.y ? v_cache : k_cache;
-  const uint4* s = base + src * block_vecs;
-  uint4* d = base + dst * block_vecs;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4* s = (blockIdx.y ? src_v : src_k) + src * block_vecs;
+  uint4* d = (blockIdx.y ? dst_v : dst_k) + dst * block_vecs;
   constexpr int kUnroll = 4;
   int64_t i = threadIdx.x;
   for (; i + (kUnroll - 1) * 256 < block_vecs; i += kUnroll * 256) {
@@ -106,10 +116,37 @@ pa_status pa_copy_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, void* 
                     desc->num_blocks);
   const int64_t block_vecs = (int64_t)desc->num_kv_heads * desc->block_size * desc->head_dim *
                              pa::elem_bytes(desc->dtype) / 16;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, (hipStream_t)stream,
-                     src_dst_pairs, (uint4*)k_cache, (uint4*)v_cache, desc->num_blocks,
+  hipLaunchKernelGGL(move_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, (hipStream_t)stream,
+                     src_dst_pairs, (const uint4*)k_cache, (const uint4*)v_cache,
+                     desc->num_blocks, (uint4*)k_cache, (uint4*)v_cache, desc->num_blocks,
                      block_vecs);
   return check_launch("pa_copy_blocks");
+}
+
+pa_status pa_swap_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, const void* src_k,
+                         const void* src_v, int32_t src_num_blocks, void* dst_k, void* dst_v,
+                         int32_t dst_num_blocks, const pa_cache_desc* desc, void* stream) {
+  pa_status st = pa::check_desc(desc);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_pairs %d < 0", num_pairs);
+  if (src_num_blocks < 1 || dst_num_blocks < 1)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "src_num_blocks %d / dst_num_blocks %d",
+                    src_num_blocks, dst_num_blocks);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_dst_pairs || !src_k || !src_v || !dst_k || !dst_v)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!pa::aligned(src_k, 16) || !pa::aligned(src_v, 16) || !pa::aligned(dst_k, 16) ||
+      !pa::aligned(dst_v, 16) || !pa::aligned(src_dst_pairs, 4))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  if (num_pairs > dst_num_blocks)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_pairs %d > dst_num_blocks %d", num_pairs,
+                    dst_num_blocks);
+  const int64_t block_vecs = (int64_t)desc->num_kv_heads * desc->block_size * desc->head_dim *
+                             pa::elem_bytes(desc->dtype) / 16;
+  hipLaunchKernelGGL(move_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, (hipStream_t)stream,
+                     src_dst_pairs, (const uint4*)src_k, (const uint4*)src_v, src_num_blocks,
+                     (uint4*)dst_k, (uint4*)dst_v, dst_num_blocks, block_vecs);
+  return check_launch("pa_swap_blocks");
 }
 
 }  // extern "C"

@@ -189,26 +189,30 @@ def _state(x, n):
 
 class LockstepMachine(RuleBasedStateMachine):
     """The same random operations on the oracle and the C allocator must give
-    bit-identical slots, copy pairs, errors, free-list order, counts and tables."""
+    bit-identical slots, copy and swap pairs, errors, free-list orders (device
+    and host), counts and tables."""
 
-    N, BS = 20, 4
+    N, BS, NH = 20, 4, 12
 
     def __init__(self):
         super().__init__()
-        order = np.random.default_rng(3).permutation(self.N)
+        rng = np.random.default_rng(3)
+        order, horder = rng.permutation(self.N), rng.permutation(self.NH)
         self.o = oa.BlockAllocator(self.N, self.BS, order)
         self.c = pa.Allocator(self.N, self.BS, order)
+        self.o.add_host_pool(self.NH, horder)
+        self.c.add_host_pool(self.NH, horder)
         self.next_id = 100
         self.ids = []
 
-    def _both(self, name, *args):
+    def _both(self, name, *args, cname=None):
         try:
             ro = getattr(self.o, name)(*args)
             eo = None
         except oa.AllocatorError as e:
             ro, eo = None, e.status
         try:
-            rc = getattr(self.c, name)(*args)
+            rc = getattr(self.c, cname or name)(*args)
             ec = None
         except pa.PagedAttentionError as e:
             rc, ec = None, e.status_name
@@ -254,16 +258,35 @@ class LockstepMachine(RuleBasedStateMachine):
         self._both("seq_free", s)
         self._sync_ids()
 
+    @precondition(lambda self: self.ids)
+    @rule(data=st.data())
+    def swap_out(self, data):
+        s = data.draw(st.sampled_from(self.ids))
+        ro, rc = self._both("swap_out", s, cname="seq_swap_out")
+        if ro is not None:
+            assert [list(p) for p in ro] == rc.tolist()
+
+    @precondition(lambda self: self.ids)
+    @rule(data=st.data())
+    def swap_in(self, data):
+        s = data.draw(st.sampled_from(self.ids))
+        ro, rc = self._both("swap_in", s, cname="seq_swap_in")
+        if ro is not None:
+            assert [list(p) for p in ro] == rc.tolist()
+
     @invariant()
     def same_state(self):
         assert _state(self.o, self.N) == _state(self.c, self.N)
+        assert self.o.host_free_list() == self.c.host_free_list()
         for s in self.o.seq_ids():
             assert self.o.seq_block_table(s) == self.c.seq_block_table(s)
             assert self.o.seq_num_tokens(s) == self.c.seq_num_tokens(s)
-        if self.ids:
-            maxb = max(1, max(len(self.o.seq_block_table(s)) for s in self.ids))
-            to, lo = self.o.block_tables(self.ids, maxb)
-            tc, lc = self.c.build_block_tables(self.ids, maxb)
+            assert self.o.seq_is_swapped(s) == self.c.seq_is_swapped(s)
+        live = [s for s in self.ids if not self.o.seq_is_swapped(s)]
+        if live:
+            maxb = max(1, max(len(self.o.seq_block_table(s)) for s in live))
+            to, lo = self.o.block_tables(live, maxb)
+            tc, lc = self.c.build_block_tables(live, maxb)
             assert np.array_equal(np.array(to, np.int32), tc) and list(lo) == lc.tolist()
 
 
@@ -313,3 +336,55 @@ def test_workload_scripts_bit_exact(name, make):
         assert len(lc[-1][1]) == 127
     if name == "prefix2048":
         assert len(lc[-1][1]) == 0
+
+
+def test_swap_pins_on_c_allocator():
+    """The oracle's swap pins, run on the C allocator."""
+    import test_oracle_swap as ts
+
+    class C(pa.Allocator):
+        def swap_out(self, seq_id):
+            return [tuple(p) for p in self.seq_swap_out(seq_id).tolist()]
+
+        def swap_in(self, seq_id):
+            return [tuple(p) for p in self.seq_swap_in(seq_id).tolist()]
+
+        def block_tables(self, seq_ids, max_blocks):
+            t, l = self.build_block_tables(seq_ids, max_blocks)
+            return t.tolist(), l.tolist()
+
+        def seq_ids(self):
+            return sorted(self._ids)
+
+        def seq_create(self, s):
+            super().seq_create(s)
+            self._ids = getattr(self, "_ids", set()) | {s}
+
+        def seq_fork(self, p, c):
+            super().seq_fork(p, c)
+            self._ids = self._ids | {c}
+
+        def seq_free(self, s):
+            super().seq_free(s)
+            self._ids = self._ids - {s}
+
+        def seq_reserve(self, ids, ns, cow_cap=None):
+            s, p = super().seq_reserve(ids, ns, cow_cap)
+            return s.tolist(), [tuple(x) for x in p.tolist()]
+
+    errs = {"OUT_OF_BLOCKS": ts.OutOfBlocks, "INVALID_ARGUMENT": ts.InvalidArgument}
+
+    class Wrapped(C):
+        def __getattribute__(self, name):
+            attr = super().__getattribute__(name)
+            if callable(attr) and not name.startswith("_") and name not in ("close",):
+                def call(*a, **k):
+                    try:
+                        return attr(*a, **k)
+                    except pa.PagedAttentionError as e:
+                        raise errs.get(e.status_name, AssertionError)(str(e)) from e
+                return call
+            return attr
+
+    for pin in ts.SWAP_PINS:
+        pin(Wrapped)
