@@ -65,6 +65,27 @@ CPU memory or dropped and recomputed later in one prefill pass].  Readings:
   A swapped-out sequence cannot reserve, fork or build a table; freeing it
   returns its host blocks.  The drop-and-recompute path needs no new state:
   free the sequence, create it again, reserve its tokens and prefill.
+
+Automatic prefix caching [P3, Trade-offs and edge cases, fourth point: full
+blocks are hashed and the least recently used are evicted; P1, Common
+questions: a runtime short of blocks may evict cached prefixes].  Readings:
+
+* A full block's key is a chained 64-bit FNV-1a hash: of the parent block's
+  key (0 for block 0) as 8 little-endian bytes, then the block's token ids
+  as 4-byte little-endian integers.  A hit also compares the stored parent
+  key and token ids, so a hash collision cannot alias two prefixes.
+* Keys come from token ids the caller registers for an empty sequence
+  (``match_prefix``, normally the prompt); blocks of tokens it never
+  registered (generated tokens) are not cached.  A block is entered in the
+  cache when it becomes full during a reserve; the first block to hold a
+  key keeps it.
+* ``match_prefix`` takes the longest run of cached blocks from block 0, at
+  most ``(n - 1) // bs`` of them so that at least one token is computed,
+  and sets the sequence's length to the tokens they hold.
+* A cached block whose count drops to zero is not freed but queued as
+  evictable, most recently released last; a hit takes it back.  Blocks are
+  taken from the free stack first, and only when it is empty is the least
+  recently used cached block evicted (its key dropped).
 """
 
 from __future__ import annotations
@@ -108,6 +129,11 @@ class BlockAllocator:
         self._ntok: dict[int, int] = {}
         self._host_free: list[int] | None = None  # host stack, top at the end
         self._swapped: set[int] = set()
+        self._pc = False                   # prefix caching on
+        self._block_of: dict[int, int] = {}    # key -> cached block
+        self._key_of: dict[int, tuple] = {}    # cached block -> (key, parent key, tokens)
+        self._lru: list[int] = []          # evictable cached blocks, next evicted first
+        self._keys: dict[int, list] = {}   # seq -> [(key, parent key, tokens)] per full block
 
     # ------------------------------------------------------------------ state
     def num_free(self) -> int:
@@ -133,6 +159,18 @@ class BlockAllocator:
     def seq_ids(self) -> list[int]:
         return sorted(self._table)
 
+    def num_cached(self) -> int:
+        return len(self._lru)
+
+    def cached_list(self) -> list[int]:
+        """Evictable cached blocks, the one evicted next first."""
+        return list(self._lru)
+
+    def block_key(self, block: int):
+        """The key of a cached block, or None."""
+        k = self._key_of.get(block)
+        return None if k is None else k[0]
+
     def num_free_host(self) -> int:
         return -1 if self._host_free is None else len(self._host_free)
 
@@ -144,6 +182,49 @@ class BlockAllocator:
     def seq_is_swapped(self, seq_id: int) -> bool:
         self._need(seq_id)
         return seq_id in self._swapped
+
+    # --------------------------------------------------------- prefix cache
+    def enable_prefix_cache(self) -> None:
+        self._pc = True
+
+    def match_prefix(self, seq_id: int, tokens) -> int:
+        """Registers the token ids of an empty sequence and takes the cached
+        blocks of its longest cached prefix; returns the tokens they hold."""
+        self._need(seq_id)
+        if not self._pc:
+            raise InvalidArgument("prefix cache is off")
+        if seq_id in self._swapped or self._table[seq_id] or self._ntok[seq_id]:
+            raise InvalidArgument("sequence is not empty")
+        toks = [int(t) for t in tokens]
+        bs = self.block_size
+        keys, parent = [], 0
+        for i in range(len(toks) // bs):
+            blk_toks = tuple(toks[i * bs:(i + 1) * bs])
+            key = block_key(parent, blk_toks)
+            keys.append((key, parent, blk_toks))
+            parent = key
+        self._keys[seq_id] = keys
+        hits = 0
+        for key, parent, blk_toks in keys[:(len(toks) - 1) // bs if toks else 0]:
+            blk = self._block_of.get(key)
+            if blk is None or self._key_of[blk] != (key, parent, blk_toks):
+                break
+            if self._rc[blk] == 0:
+                self._lru.remove(blk)
+            self._rc[blk] += 1
+            self._table[seq_id].append(blk)
+            hits += 1
+        self._ntok[seq_id] = hits * bs
+        return hits * bs
+
+    def _release(self, blk: int) -> None:
+        """One reference fewer; at zero a cached block queues for eviction."""
+        self._rc[blk] -= 1
+        if self._rc[blk] == 0:
+            if blk in self._key_of:
+                self._lru.append(blk)
+            else:
+                self._free.append(blk)
 
     # ------------------------------------------------------------ host pool
     def add_host_pool(self, num_host_blocks: int, free_order=None) -> None:
@@ -170,9 +251,7 @@ class BlockAllocator:
         host = [self._host_free.pop() for _ in table]
         pairs = list(zip(table, host))
         for blk in reversed(table):
-            self._rc[blk] -= 1
-            if self._rc[blk] == 0:
-                self._free.append(blk)
+            self._release(blk)
         self._table[seq_id] = host
         self._swapped.add(seq_id)
         return pairs
@@ -183,9 +262,9 @@ class BlockAllocator:
         if seq_id not in self._swapped:
             raise InvalidArgument("sequence is not swapped out")
         host = self._table[seq_id]
-        if len(host) > len(self._free):
+        if len(host) > len(self._free) + len(self._lru):
             raise OutOfBlocks("no free block")
-        dev = [self._free.pop() for _ in host]
+        dev = [self._pop() for _ in host]
         for blk in dev:
             self._rc[blk] = 1
         pairs = list(zip(host, dev))
@@ -211,6 +290,8 @@ class BlockAllocator:
             raise InvalidArgument("child exists")
         self._table[child] = list(self._table[parent])
         self._ntok[child] = self._ntok[parent]
+        if parent in self._keys:
+            self._keys[child] = list(self._keys[parent])
         for blk in self._table[child]:
             self._rc[blk] += 1
 
@@ -222,11 +303,10 @@ class BlockAllocator:
             self._swapped.discard(seq_id)
         else:
             for blk in reversed(self._table[seq_id]):
-                self._rc[blk] -= 1
-                if self._rc[blk] == 0:
-                    self._free.append(blk)
+                self._release(blk)
         del self._table[seq_id]
         del self._ntok[seq_id]
+        self._keys.pop(seq_id, None)
 
     def seq_reserve(self, seq_ids, n_new, cow_cap=None):
         """Give ``n_new[i]`` new token slots to ``seq_ids[i]``, in call order.
@@ -252,13 +332,15 @@ class BlockAllocator:
             seen.add(sid)
 
         saved = (list(self._free), list(self._rc),
-                 copy.deepcopy(self._table), dict(self._ntok))
+                 copy.deepcopy(self._table), dict(self._ntok), list(self._lru),
+                 dict(self._block_of), dict(self._key_of))
         try:
             slots, pairs = self._reserve(seq_ids, n_new)
             if cow_cap is not None and len(pairs) > cow_cap:
                 raise InvalidArgument("copy-on-write pair capacity too small")
         except AllocatorError:
-            self._free, self._rc, self._table, self._ntok = saved
+            (self._free, self._rc, self._table, self._ntok, self._lru, self._block_of,
+             self._key_of) = saved
             raise
         return slots, pairs
 
@@ -283,9 +365,13 @@ class BlockAllocator:
             raise UnknownSeq(f"unknown sequence {seq_id}")
 
     def _pop(self) -> int:
-        if not self._free:
-            raise OutOfBlocks("no free block")
-        return self._free.pop()
+        if self._free:
+            return self._free.pop()
+        if self._lru:  # evict the least recently used cached block
+            blk = self._lru.pop(0)
+            del self._block_of[self._key_of.pop(blk)[0]]
+            return blk
+        raise OutOfBlocks("no free block")
 
     def _reserve(self, seq_ids, n_new):
         bs = self.block_size
@@ -310,4 +396,29 @@ class BlockAllocator:
                     pairs.append((src, dst))
                 slots.append(table[lb] * bs + off)
                 self._ntok[sid] = pos + 1
+                keys = self._keys.get(sid)
+                if off == bs - 1 and keys is not None and lb < len(keys):
+                    key = keys[lb][0]
+                    if key not in self._block_of:  # the block is full: cache it
+                        self._block_of[key] = table[lb]
+                        self._key_of[table[lb]] = keys[lb]
         return slots, pairs
+
+
+FNV64_OFFSET = 0xCBF29CE484222325
+FNV64_PRIME = 0x100000001B3
+
+
+def fnv1a64(data: bytes, h: int = FNV64_OFFSET) -> int:
+    """64-bit FNV-1a (Fowler, Noll, Vo): for each byte, xor then multiply."""
+    for byte in data:
+        h = ((h ^ byte) * FNV64_PRIME) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def block_key(parent: int, tokens) -> int:
+    """Key of a full block: FNV-1a over the parent key (8 bytes LE) and the
+    token ids (4 bytes LE each)."""
+    data = int(parent).to_bytes(8, "little") + b"".join(
+        int(t).to_bytes(4, "little", signed=True) for t in tokens)
+    return fnv1a64(data)
