@@ -68,7 +68,8 @@ def parse():
                         "block_size_sweep_bs{8,16,32,128}, prefix_sharing_p{2056,2048}: pa_decode "
                         "alone on that workload's batch (kernel leg only); llama3_8b_prefill, "
                         "llama3_8b_chunked_prefill_cN: pa_prefill alone on the worked batch; "
-                        "swap_llama3_8b: pa_swap_blocks out to pinned host memory and back")
+                        "swap_llama3_8b: pa_swap_blocks out to pinned host memory and back; "
+                        "prefix_cache_p2056: prefill with and without the prefix cache")
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying a captured HIP graph")
     return p.parse_args()
@@ -436,6 +437,97 @@ def swap_workload(args):
                                                 "launch per direction"}}), flush=True)
 
 
+def prefix_cache_workload(args):
+    """Prefix caching on the prefix-sharing requests: 128 prompts of a shared
+    2,056-token system prompt plus each request's own suffix (uniform 0-512
+    tokens plus one), at the Llama-3-8B head layout.  Without the cache every
+    prompt is prefilled whole; with it, a first request fills the prompt's
+    blocks, and each request then takes its 128 cached blocks
+    (pa_seq_match_prefix) and prefills only the rest, as one chunked-prefill
+    call against the shared blocks.  Reports both pa_prefill times (graph
+    replay) and the host cost of the lookups."""
+    import torch
+
+    import paged_kv_cache_338_amd as pa
+    import workloads as W
+
+    dev = "cuda:0"
+    w = W.prefix_sharing(with_values=False)
+    P, bs, H_q, H_kv, D = w.notes["prefix_len"], w.block_size, w.num_q_heads, w.num_kv_heads, w.head_dim
+    suffix = [x + 1 for x in w.notes["suffix"]]
+    rng = np.random.default_rng(w.seed)
+    prompt = rng.integers(0, 32000, P).astype(np.int32)
+    prompts = [np.concatenate([prompt, rng.integers(0, 32000, n).astype(np.int32)])
+               for n in suffix]
+    lens = np.array([len(t) for t in prompts], np.int32)
+    B = len(prompts)
+    nb = int(sum(-(-L // bs) for L in lens) * 1.1) + 64
+    shape = (nb, H_kv, bs, D)
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    kp = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+    vp = torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16)
+
+    def prefill_us(alloc, ids, nq):
+        maxb = max(len(alloc.seq_block_table(s)) for s in ids)
+        tables, ln = alloc.build_block_tables(ids, maxb)
+        qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+        T = int(qs[-1])
+        q = torch.randn((T, H_q, D), generator=gen, device=dev).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        td, ld, qsd = (torch.from_numpy(x).to(dev) for x in (tables, ln, qs))
+        us = replay_timed(lambda: [pa.prepare_prefill(q, kp, vp, td, ld, qsd, bs, w.scale, out)],
+                          args.kernel_reps)
+        return us, prefill_flops(ln, nq, H_q, D), T
+
+    # Without the cache: every prompt prefilled whole.
+    order = rng.permutation(nb)
+    a0 = pa.Allocator(nb, bs, order)
+    for i in range(B):
+        a0.seq_create(i)
+        a0.seq_reserve([i], [int(lens[i])])
+    us_full, fl_full, T_full = prefill_us(a0, list(range(B)), lens)
+    del a0
+    # With the cache: one request fills the prompt, then each request reuses it.
+    a1 = pa.Allocator(nb, bs, order)
+    a1.enable_prefix_cache()
+    a1.seq_create(-1)
+    a1.match_prefix(-1, prompt)
+    a1.seq_reserve([-1], [P])
+    a1.seq_free(-1)
+    t0 = time.perf_counter()
+    hits = []
+    for i, toks in enumerate(prompts):
+        a1.seq_create(i)
+        h = a1.match_prefix(i, toks)
+        a1.seq_reserve([i], [len(toks) - h])
+        hits.append(h)
+    host_us = (time.perf_counter() - t0) * 1e6 / B
+    nq = lens - np.array(hits, np.int32)
+    us_cached, fl_cached, T_cached = prefill_us(a1, list(range(B)), nq)
+    log(f"prefix cache: {B} requests, prompt {P} + suffixes: whole prompts {T_full} queries "
+        f"{us_full:.1f} us; cached prefix (hits {min(hits)}-{max(hits)} tokens) {T_cached} queries "
+        f"{us_cached:.1f} us ({us_full / us_cached:.2f}x); lookup + reserve {host_us:.1f} us/request")
+    tfs = fl_cached / (us_cached * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": "prefix-cached prefill time per call (us), 128 requests sharing a 2,056-token "
+                  "prompt, Llama-3-8B heads", "value": round(us_cached, 2), "unit": "us",
+        "n_gpus": 1, "steps": args.kernel_reps, "warmup": 1,
+        "ms_per_step": round(us_cached / 1e3, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefix_cache_p2056: pa_seq_match_prefix + suffix-only pa_prefill "
+                               "vs whole-prompt pa_prefill, graph replay",
+                   "requests": B, "prompt_tokens": P, "query_tokens_whole": T_full,
+                   "query_tokens_cached": T_cached, "us_whole_prompts": round(us_full, 2),
+                   "us_cached_prefix": round(us_cached, 2),
+                   "speedup": round(us_full / us_cached, 3),
+                   "host_us_per_request": round(host_us, 2),
+                   "cached_tokens_per_request": int(min(hits))},
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "pa_prefill over the cached prefix",
+                     "algorithmic_flops_per_call": fl_cached}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -450,6 +542,8 @@ def main():
             prefill_workload(args)
         elif args.workload == "swap_llama3_8b":
             swap_workload(args)
+        elif args.workload == "prefix_cache_p2056":
+            prefix_cache_workload(args)
         else:
             other_workload(args)
         return

@@ -310,6 +310,36 @@ pa_status pa_seq_swap_out(pa_allocator* alloc, int64_t seq_id, int32_t* pairs_ou
 pa_status pa_seq_swap_in(pa_allocator* alloc, int64_t seq_id, int32_t* pairs_out, int32_t cap,
                          int32_t* num_pairs_out);
 
+/* Automatic prefix caching [P3 Trade-offs and edge cases, fourth point: full
+ * blocks are hashed and the least recently used are evicted; P1 Common
+ * questions: cached prefixes may be evicted under memory pressure].
+ * Turns it on (idempotent).  From then on a block whose count drops to zero
+ * and that holds a key waits on an LRU list instead of the free list; a
+ * block request takes the free list first, then evicts the least recently
+ * released cached block (its key is dropped). */
+pa_status pa_allocator_enable_prefix_cache(pa_allocator* alloc);
+
+/* Registers the token ids of an empty sequence (normally its prompt) and
+ * takes the cached blocks of its longest cached prefix.  Full block i of
+ * tokens has the key FNV-1a-64(key(i-1) as 8 little-endian bytes, then its
+ * bs token ids as 4-byte little-endian integers), key(-1) = 0; a hit also
+ * matches the stored parent key and token ids.  At most (n - 1) / bs blocks
+ * are taken (at least one token is left to compute), in order from block 0
+ * up to the first miss; each taken block's count + 1 (off the LRU list if it
+ * was 0).  The sequence's length becomes the tokens they hold
+ * (*num_cached_out); the caller reserves and fills the rest, and each
+ * registered block is cached when a reserve fills it (the first block to
+ * hold a key keeps it).  tokens: host int32 [n].  Errors: UNKNOWN_SEQ;
+ * INVALID_ARGUMENT if the cache is off or the sequence is not empty. */
+pa_status pa_seq_match_prefix(pa_allocator* alloc, int64_t seq_id, const int32_t* tokens,
+                              int32_t n, int32_t* num_cached_out);
+
+/* Evictable cached blocks (count 0), and their list, the one evicted next
+ * first (as pa_allocator_free_list). */
+int32_t pa_allocator_num_cached(const pa_allocator* alloc);
+pa_status pa_allocator_cached_list(const pa_allocator* alloc, int32_t* out, int32_t cap,
+                                   int32_t* len);
+
 /* *out = 1 if seq_id is swapped out, else 0. */
 pa_status pa_seq_is_swapped(const pa_allocator* alloc, int64_t seq_id, int32_t* out);
 /* Free host blocks (-1 without a host pool), and the host stack, the block

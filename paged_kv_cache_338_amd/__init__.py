@@ -90,6 +90,10 @@ SIGNATURES = {
     "pa_seq_is_swapped": (_I32, [_P, _I64, _PI32]),
     "pa_allocator_num_free_host": (_I32, [_P]),
     "pa_allocator_host_free_list": (_I32, [_P, _PI32, _I32, _PI32]),
+    "pa_allocator_enable_prefix_cache": (_I32, [_P]),
+    "pa_seq_match_prefix": (_I32, [_P, _I64, _PI32, _I32, _PI32]),
+    "pa_allocator_num_cached": (_I32, [_P]),
+    "pa_allocator_cached_list": (_I32, [_P, _PI32, _I32, _PI32]),
 }
 
 _lib = None
@@ -440,6 +444,30 @@ class Allocator:
     def seq_swap_in(self, seq_id):
         """Returns int32 [n, 2] (host block, device block) pairs."""
         return self._swap(self._lib.pa_seq_swap_in, seq_id)
+
+    # -------------------------------------------------------- prefix cache
+    def enable_prefix_cache(self):
+        _check(self._lib.pa_allocator_enable_prefix_cache(self._h))
+
+    def match_prefix(self, seq_id, tokens):
+        """Registers the tokens of an empty sequence; returns the cached tokens taken."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pa_seq_match_prefix(self._h, int(seq_id),
+                                             _ptr(t, ctypes.c_int32) if t.size else None, t.size,
+                                             ctypes.byref(n)))
+        return n.value
+
+    def num_cached(self):
+        return self._lib.pa_allocator_num_cached(self._h)
+
+    def cached_list(self):
+        n = self.num_cached()
+        out = np.empty(max(n, 1), np.int32)
+        ln = ctypes.c_int32(0)
+        _check(self._lib.pa_allocator_cached_list(self._h, _ptr(out, ctypes.c_int32), out.size,
+                                                  ctypes.byref(ln)))
+        return out[:ln.value].tolist()
 
     def seq_is_swapped(self, seq_id):
         v = ctypes.c_int32(0)

@@ -17,12 +17,24 @@
 // other sharers); swap-in is the reverse, into private device blocks.  Both
 // check the target pool first, so they change nothing when it is short.
 //
+// Automatic prefix caching (clozo.ai page, Trade-offs and edge cases, fourth
+// point: full blocks are hashed, the least recently used are evicted): a
+// full block's key is a chained 64-bit FNV-1a hash of its parent's key and
+// its token ids, verified on a hit against the stored parent key and
+// tokens.  Token ids come from pa_seq_match_prefix (normally the prompt);
+// a block is cached when it becomes full during a reserve.  Released
+// cached blocks wait on an LRU list; allocation takes free blocks first and
+// then evicts the least recently used cached block.
+//
 // Every entry point gives the strong guarantee: pa_seq_reserve keeps an undo
 // log while it walks the tokens and replays it backwards when it runs out of
 // blocks or out of room for copy pairs, so a failed call leaves the free
 // stack order, counts and tables exactly as they were.
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
+#include <iterator>
+#include <list>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -32,15 +44,42 @@
 
 namespace {
 
+// Key of one full block of registered tokens.
+struct BlockKey {
+  uint64_t key = 0;
+  uint64_t parent = 0;
+  std::vector<int32_t> tokens;
+};
+
 struct Sequence {
   std::vector<int32_t> table;  // logical block -> physical block (host block when swapped)
   int32_t num_tokens = 0;
   bool swapped = false;
+  std::vector<BlockKey> keys;  // per full block of the registered tokens
 };
+
+// 64-bit FNV-1a (Fowler, Noll, Vo): per byte, xor then multiply.
+constexpr uint64_t kFnvOffset = 0xCBF29CE484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001B3ull;
+
+uint64_t fnv1a64(const uint8_t* p, size_t n, uint64_t h = kFnvOffset) {
+  for (size_t i = 0; i < n; ++i) h = (h ^ p[i]) * kFnvPrime;
+  return h;
+}
+
+// Parent key as 8 little-endian bytes, then each token as 4 (the x86-64 and
+// gfx950 hosts are little-endian, so the in-memory bytes are those bytes).
+uint64_t block_key(uint64_t parent, const int32_t* tokens, int32_t n) {
+  uint8_t pb[8];
+  std::memcpy(pb, &parent, 8);
+  const uint64_t h = fnv1a64(pb, 8);
+  return fnv1a64(reinterpret_cast<const uint8_t*>(tokens), sizeof(int32_t) * (size_t)n, h);
+}
 
 // One reversible change made by a reserve call.
 struct Undo {
-  enum Kind : uint8_t { kPop, kRefcount, kTableAppend, kTableSet, kTokens } kind;
+  enum Kind : uint8_t { kPop, kRefcount, kTableAppend, kTableSet, kTokens, kEvict,
+                        kRegister } kind;
   Sequence* seq;
   int32_t a;  // block (kPop, kRefcount), logical index (kTableSet)
   int32_t b;  // old value (kRefcount, kTableSet, kTokens)
@@ -58,6 +97,14 @@ struct pa_allocator {
   bool has_host = false;
   int32_t num_host_blocks = 0;
   std::vector<int32_t> host_free;  // top at back()
+  // Prefix cache: per block whether it holds a key (and which), the key ->
+  // block map, and the evictable (count 0) cached blocks, next evicted first.
+  bool prefix_cache = false;
+  std::vector<uint8_t> cached;
+  std::vector<BlockKey> bkey;
+  std::unordered_map<uint64_t, int32_t> block_of;
+  std::list<int32_t> lru;
+  std::vector<std::list<int32_t>::iterator> lru_pos;
 
   Sequence* find(int64_t id) {
     auto it = seqs.find(id);
@@ -76,17 +123,65 @@ struct pa_allocator {
         case Undo::kTableAppend: it->seq->table.pop_back(); break;
         case Undo::kTableSet: it->seq->table[it->a] = it->b; break;
         case Undo::kTokens: it->seq->num_tokens = it->b; break;
+        case Undo::kEvict:
+          cached[it->a] = 1;
+          block_of[bkey[it->a].key] = it->a;
+          lru.push_front(it->a);
+          lru_pos[it->a] = lru.begin();
+          break;
+        case Undo::kRegister:
+          cached[it->a] = 0;
+          block_of.erase(bkey[it->a].key);
+          break;
       }
     }
     undo.clear();
   }
 
   bool pop(int32_t* blk) {
-    if (free_stack.empty()) return false;
-    *blk = free_stack.back();
-    free_stack.pop_back();
-    undo.push_back({Undo::kPop, nullptr, *blk, 0});
-    return true;
+    if (!free_stack.empty()) {
+      *blk = free_stack.back();
+      free_stack.pop_back();
+      undo.push_back({Undo::kPop, nullptr, *blk, 0});
+      return true;
+    }
+    if (prefix_cache && !lru.empty()) {  // evict the least recently used cached block
+      *blk = lru.front();
+      lru.pop_front();
+      cached[*blk] = 0;
+      block_of.erase(bkey[*blk].key);
+      undo.push_back({Undo::kEvict, nullptr, *blk, 0});
+      return true;
+    }
+    return false;
+  }
+
+  int64_t available() const {
+    return static_cast<int64_t>(free_stack.size()) + (prefix_cache ? lru.size() : 0);
+  }
+
+  // One reference fewer; at zero a cached block waits on the LRU list.
+  void release(int32_t blk) {
+    if (--refcount[blk] != 0) return;
+    if (prefix_cache && cached[blk]) {
+      lru.push_back(blk);
+      lru_pos[blk] = std::prev(lru.end());
+    } else {
+      free_stack.push_back(blk);
+    }
+  }
+
+  // Block lb of s just became full: cache it under its key if it has one
+  // and the key is not held by another block.
+  void maybe_register(Sequence* s, int32_t lb) {
+    if (!prefix_cache || lb >= static_cast<int32_t>(s->keys.size())) return;
+    const BlockKey& k = s->keys[lb];
+    if (block_of.count(k.key)) return;
+    const int32_t blk = s->table[lb];
+    bkey[blk] = k;
+    cached[blk] = 1;
+    block_of[k.key] = blk;
+    undo.push_back({Undo::kRegister, nullptr, blk, 0});
   }
 
   void set_refcount(int32_t blk, int32_t value) {
@@ -163,9 +258,7 @@ pa_status pa_seq_free(pa_allocator* alloc, int64_t seq_id) {
   if (it->second.swapped) {
     for (auto r = t.rbegin(); r != t.rend(); ++r) alloc->host_free.push_back(*r);
   } else {
-    for (auto r = t.rbegin(); r != t.rend(); ++r) {
-      if (--alloc->refcount[*r] == 0) alloc->free_stack.push_back(*r);
-    }
+    for (auto r = t.rbegin(); r != t.rend(); ++r) alloc->release(*r);
   }
   alloc->seqs.erase(it);
   return PA_OK;
@@ -245,6 +338,7 @@ pa_status pa_seq_reserve(pa_allocator* alloc, const int64_t* seq_ids, const int3
       }
       slot_mapping_out[t++] = static_cast<int64_t>(s->table[lb]) * bs + off;
       s->num_tokens = pos + 1;
+      if (off == bs - 1) alloc->maybe_register(s, lb);
     }
   }
   if (pairs > cow_cap) {
@@ -331,10 +425,7 @@ pa_status pa_seq_swap_out(pa_allocator* alloc, int64_t seq_id, int32_t* pairs_ou
     pairs_out[2 * i] = s->table[i];
     pairs_out[2 * i + 1] = h;
   }
-  for (int32_t i = n - 1; i >= 0; --i) {
-    const int32_t blk = s->table[i];
-    if (--alloc->refcount[blk] == 0) alloc->free_stack.push_back(blk);
-  }
+  for (int32_t i = n - 1; i >= 0; --i) alloc->release(s->table[i]);
   for (int32_t i = 0; i < n; ++i) s->table[i] = pairs_out[2 * i + 1];
   s->swapped = true;
   if (num_pairs_out) *num_pairs_out = n;
@@ -350,22 +441,88 @@ pa_status pa_seq_swap_in(pa_allocator* alloc, int64_t seq_id, int32_t* pairs_out
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is not swapped out",
                     (long long)seq_id);
   const int32_t n = static_cast<int32_t>(s->table.size());
-  if (n > static_cast<int32_t>(alloc->free_stack.size()))
-    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "no free block (%zu free, %d needed)",
-                    alloc->free_stack.size(), n);
+  if (n > alloc->available())
+    return pa::fail(PA_ERR_OUT_OF_BLOCKS, "no free block (%lld free, %d needed)",
+                    (long long)alloc->available(), n);
   if (cap < n) return pa::fail(PA_ERR_INVALID_ARGUMENT, "cap %d < %d pairs", cap, n);
   if (n > 0 && !pairs_out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "pairs_out is NULL");
   for (int32_t i = 0; i < n; ++i) {
-    const int32_t d = alloc->free_stack.back();
-    alloc->free_stack.pop_back();
+    int32_t d = 0;
+    alloc->pop(&d);  // cannot fail: checked above
     alloc->refcount[d] = 1;
     pairs_out[2 * i] = s->table[i];
     pairs_out[2 * i + 1] = d;
   }
+  alloc->undo.clear();
   for (int32_t i = n - 1; i >= 0; --i) alloc->host_free.push_back(s->table[i]);
   for (int32_t i = 0; i < n; ++i) s->table[i] = pairs_out[2 * i + 1];
   s->swapped = false;
   if (num_pairs_out) *num_pairs_out = n;
+  return PA_OK;
+}
+
+pa_status pa_allocator_enable_prefix_cache(pa_allocator* alloc) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  if (!alloc->prefix_cache) {
+    alloc->prefix_cache = true;
+    alloc->cached.assign(alloc->num_blocks, 0);
+    alloc->bkey.assign(alloc->num_blocks, BlockKey{});
+    alloc->lru_pos.assign(alloc->num_blocks, alloc->lru.end());
+  }
+  return PA_OK;
+}
+
+pa_status pa_seq_match_prefix(pa_allocator* alloc, int64_t seq_id, const int32_t* tokens,
+                              int32_t n, int32_t* num_cached_out) {
+  if (!alloc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "allocator is NULL");
+  Sequence* s = alloc->find(seq_id);
+  if (!s) return pa::fail(PA_ERR_UNKNOWN_SEQ, "unknown sequence %lld", (long long)seq_id);
+  if (!alloc->prefix_cache) return pa::fail(PA_ERR_INVALID_ARGUMENT, "prefix cache is off");
+  if (s->swapped || !s->table.empty() || s->num_tokens != 0)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "sequence %lld is not empty", (long long)seq_id);
+  if (n < 0 || (n > 0 && !tokens))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "n = %d / tokens is NULL", n);
+  const int32_t bs = alloc->block_size;
+  const int32_t nfull = n / bs;
+  std::vector<BlockKey> keys(nfull);
+  uint64_t parent = 0;
+  for (int32_t i = 0; i < nfull; ++i) {
+    keys[i].parent = parent;
+    keys[i].tokens.assign(tokens + (int64_t)i * bs, tokens + (int64_t)(i + 1) * bs);
+    keys[i].key = block_key(parent, tokens + (int64_t)i * bs, bs);
+    parent = keys[i].key;
+  }
+  const int32_t max_hits = n > 0 ? (n - 1) / bs : 0;
+  int32_t hits = 0;
+  for (; hits < max_hits; ++hits) {
+    const BlockKey& k = keys[hits];
+    auto it = alloc->block_of.find(k.key);
+    if (it == alloc->block_of.end()) break;
+    const int32_t blk = it->second;
+    const BlockKey& have = alloc->bkey[blk];
+    if (have.parent != k.parent || have.tokens != k.tokens) break;
+    if (alloc->refcount[blk] == 0) alloc->lru.erase(alloc->lru_pos[blk]);
+    alloc->refcount[blk] += 1;
+    s->table.push_back(blk);
+  }
+  s->keys = std::move(keys);
+  s->num_tokens = hits * bs;
+  if (num_cached_out) *num_cached_out = hits * bs;
+  return PA_OK;
+}
+
+int32_t pa_allocator_num_cached(const pa_allocator* alloc) {
+  return alloc ? static_cast<int32_t>(alloc->lru.size()) : -1;
+}
+
+pa_status pa_allocator_cached_list(const pa_allocator* alloc, int32_t* out, int32_t cap,
+                                   int32_t* len) {
+  if (!alloc || !len) return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL argument");
+  const int32_t nc = static_cast<int32_t>(alloc->lru.size());
+  *len = nc;
+  if (cap < nc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "cap %d < %d cached blocks", cap, nc);
+  if (nc > 0 && !out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "out is NULL");
+  std::copy(alloc->lru.begin(), alloc->lru.end(), out);
   return PA_OK;
 }
 

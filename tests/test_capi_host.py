@@ -202,6 +202,8 @@ class LockstepMachine(RuleBasedStateMachine):
         self.c = pa.Allocator(self.N, self.BS, order)
         self.o.add_host_pool(self.NH, horder)
         self.c.add_host_pool(self.NH, horder)
+        self.o.enable_prefix_cache()
+        self.c.enable_prefix_cache()
         self.next_id = 100
         self.ids = []
 
@@ -258,6 +260,19 @@ class LockstepMachine(RuleBasedStateMachine):
         self._both("seq_free", s)
         self._sync_ids()
 
+    @rule(data=st.data())
+    def create_with_prompt(self, data):
+        """A new sequence whose prompt comes from a small vocabulary, so that
+        prompts repeat and share prefixes."""
+        sid = self.next_id
+        self.next_id += 1
+        toks = data.draw(st.lists(st.integers(0, 2), min_size=0, max_size=14))
+        self._both("seq_create", sid)
+        ro, rc = self._both("match_prefix", sid, toks)
+        assert ro == rc
+        self._both("seq_reserve", [sid], [len(toks) - (ro or 0)])
+        self._sync_ids()
+
     @precondition(lambda self: self.ids)
     @rule(data=st.data())
     def swap_out(self, data):
@@ -278,6 +293,7 @@ class LockstepMachine(RuleBasedStateMachine):
     def same_state(self):
         assert _state(self.o, self.N) == _state(self.c, self.N)
         assert self.o.host_free_list() == self.c.host_free_list()
+        assert self.o.cached_list() == self.c.cached_list()
         for s in self.o.seq_ids():
             assert self.o.seq_block_table(s) == self.c.seq_block_table(s)
             assert self.o.seq_num_tokens(s) == self.c.seq_num_tokens(s)
@@ -388,3 +404,33 @@ def test_swap_pins_on_c_allocator():
 
     for pin in ts.SWAP_PINS:
         pin(Wrapped)
+
+
+def test_prefix_pins_on_c_allocator():
+    """The oracle's prefix-cache pins, run on the C allocator."""
+    import test_oracle_prefix_cache as tp
+
+    errs = {"OUT_OF_BLOCKS": tp.OutOfBlocks, "INVALID_ARGUMENT": tp.InvalidArgument}
+
+    class C(pa.Allocator):
+        def __getattribute__(self, name):
+            attr = super().__getattribute__(name)
+            if callable(attr) and not name.startswith("_") and name != "close":
+                def call(*a, **k):
+                    try:
+                        r = attr(*a, **k)
+                    except pa.PagedAttentionError as e:
+                        raise errs.get(e.status_name, AssertionError)(str(e)) from e
+                    if name == "seq_reserve":
+                        return r[0].tolist(), [tuple(x) for x in r[1].tolist()]
+                    if name == "build_block_tables":
+                        return r[0].tolist(), r[1].tolist()
+                    return r
+                return call
+            return attr
+
+        def block_tables(self, seq_ids, max_blocks):
+            return self.build_block_tables(seq_ids, max_blocks)
+
+    for pin in tp.PREFIX_PINS:
+        pin(C)

@@ -1,0 +1,92 @@
+"""Prefix caching on the GPU (kernels unchanged): a request whose prompt
+starts with a cached prefix reuses those blocks and prefills only the rest,
+as a chunked prefill over the shared blocks; the result must match the
+oracle's causal attention over the whole prompt (needs a gfx950 GPU)."""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import prefill as opf
+
+pytestmark = pytest.mark.gpu
+
+BS, HKV, G, D = 16, 2, 4, 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import paged_kv_cache_338_amd as pa
+    pa.load_library()
+    yield
+
+
+def _bf16(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def test_cached_prefix_then_suffix_prefill_matches_oracle():
+    import torch
+    import paged_kv_cache_338_amd as pa
+    rng = np.random.default_rng(17)
+    nb = 200
+    vocab = 50
+    # Per token id, its K/V rows (what a model would produce at that position
+    # for this prompt; the shared prefix makes them equal across requests).
+    prompt = list(rng.integers(0, vocab, 300))
+    tails = [list(rng.integers(0, vocab, n)) for n in (37, 5, 130)]
+    toks_all = [prompt + t for t in tails]
+    pos_rows = {}
+
+    def rows_for(tokens):
+        key = tuple(tokens)
+        for i in range(len(tokens)):
+            k = key[:i + 1]
+            if k not in pos_rows:
+                pos_rows[k] = (W.round_to_bf16_bits(rng.standard_normal((HKV, D)).astype(np.float32)),
+                               W.round_to_bf16_bits(rng.standard_normal((HKV, D)).astype(np.float32)))
+        return (np.stack([pos_rows[key[:i + 1]][0] for i in range(len(tokens))]),
+                np.stack([pos_rows[key[:i + 1]][1] for i in range(len(tokens))]))
+
+    a = pa.Allocator(nb, BS, rng.permutation(nb))
+    a.enable_prefix_cache()
+    poison = np.full((nb, HKV, BS, D), W.POISON_BITS["bf16"], np.uint16)
+    kc, vc = _bf16(poison), _bf16(poison)
+    # First request: the bare prompt, prefilled whole, then finished.
+    a.seq_create(0)
+    assert a.match_prefix(0, prompt) == 0
+    slots, _ = a.seq_reserve([0], [len(prompt)])
+    k, v = rows_for(prompt)
+    pa.pa_cache_append(_bf16(k), _bf16(v), torch.from_numpy(slots.copy()).cuda(), kc, vc)
+    a.seq_free(0)
+    assert a.num_cached() == len(prompt) // BS
+    # Three requests sharing the prompt: each takes the cached blocks and
+    # appends + prefills only its own tail.
+    hits, qs = [], [0]
+    for i, toks in enumerate(toks_all, start=1):
+        a.seq_create(i)
+        h = a.match_prefix(i, toks)
+        assert h == len(prompt) // BS * BS
+        slots, _ = a.seq_reserve([i], [len(toks) - h])
+        k, v = rows_for(toks)
+        pa.pa_cache_append(_bf16(k[h:]), _bf16(v[h:]), torch.from_numpy(slots.copy()).cuda(), kc, vc)
+        hits.append(h)
+        qs.append(qs[-1] + len(toks) - h)
+    ids = [1, 2, 3]
+    tables, lens = a.build_block_tables(ids, 40)
+    assert all((tables[j, :hits[j] // BS] == tables[0, :hits[0] // BS]).all() for j in range(3))
+    q = W.round_to_bf16_bits(rng.standard_normal((qs[-1], G * HKV, D)).astype(np.float32))
+    out = torch.full((qs[-1], G * HKV, D), float("nan"), dtype=torch.bfloat16).cuda()
+    qs_np = np.array(qs, np.int32)
+    pa.pa_prefill(_bf16(q), kc, vc, torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                  torch.from_numpy(qs_np).cuda(), BS, 1 / np.sqrt(D), out)
+    torch.cuda.synchronize()
+    got = out.cpu().to(torch.float64).numpy()
+    k_np = kc.cpu().view(torch.int16).numpy().view(np.uint16)
+    v_np = vc.cpu().view(torch.int16).numpy().view(np.uint16)
+    want = opf.paged_prefill(q, k_np, v_np, tables, lens, qs_np, BS, 1 / np.sqrt(D), "bf16")
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - want).max()) <= 2e-2
