@@ -69,7 +69,9 @@ def parse():
                         "alone on that workload's batch (kernel leg only); llama3_8b_prefill, "
                         "llama3_8b_chunked_prefill_cN: pa_prefill alone on the worked batch; "
                         "swap_llama3_8b: pa_swap_blocks out to pinned host memory and back; "
-                        "prefix_cache_p2056: prefill with and without the prefix cache")
+                        "prefix_cache_p2056: prefill with and without the prefix cache; a _f16 "
+                        "suffix (llama3_8b_decode_f16, llama3_8b_prefill_f16, ...) runs a "
+                        "decode or prefill leg on fp16 pools")
     p.add_argument("--eager", action="store_true",
                    help="launch every call from Python instead of replaying a captured HIP graph")
     return p.parse_args()
@@ -213,7 +215,12 @@ def other_workload(args):
     import workloads as W
 
     name = args.workload
-    if name.startswith("block_size_sweep_bs"):
+    f16 = name.endswith("_f16")  # the same batch on IEEE fp16 pools
+    if f16:
+        name = name[:-len("_f16")]
+    if name == "llama3_8b_decode":
+        w = W.llama3_8b_decode(with_values=False)
+    elif name.startswith("block_size_sweep_bs"):
         w = W.block_size_sweep(int(name[len("block_size_sweep_bs"):]), with_values=False)
     elif name.startswith("prefix_sharing_p"):
         w = W.prefix_sharing(prefix_len=int(name[len("prefix_sharing_p"):]), with_values=False)
@@ -226,9 +233,10 @@ def other_workload(args):
     B, H_q, D = w.batch, w.num_q_heads, w.head_dim
     shape = (w.num_blocks, w.num_kv_heads, w.block_size, D)
     gen = torch.Generator(device=dev).manual_seed(w.seed)
-    kp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(args.layers)]
-    vp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(args.layers)]
-    q = torch.randn((B, H_q, D), generator=gen, device=dev).to(torch.bfloat16)
+    dt = torch.float16 if f16 else torch.bfloat16
+    kp = [torch.randn(shape, generator=gen, device=dev).to(dt) for _ in range(args.layers)]
+    vp = [torch.randn(shape, generator=gen, device=dev).to(dt) for _ in range(args.layers)]
+    q = torch.randn((B, H_q, D), generator=gen, device=dev).to(dt)
     outs = [torch.empty_like(q) for _ in range(args.layers)]
     ws = pa.decode_workspace(kp[0], B, H_q, maxb)
     td = torch.from_numpy(tables).to(dev)
@@ -238,13 +246,15 @@ def other_workload(args):
                       args.kernel_reps) / args.layers
     kv = int(lens.sum()) * kv_bytes_per_token(w)
     gbs = kv / (us * 1e-6) / 1e9
-    log(f"{name}: B={B} tokens={int(lens.sum())} maxb={maxb}: {us:.2f} us/call, {gbs:.0f} GB/s")
+    log(f"{args.workload}: B={B} tokens={int(lens.sum())} maxb={maxb}: {us:.2f} us/call, "
+        f"{gbs:.0f} GB/s")
     print(json.dumps({
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.kernel_reps * args.layers, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{name}: pa_decode alone, {args.layers} layer pools, graph replay",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if f16 else "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: pa_decode alone, {args.layers} layer pools, "
+                               "graph replay",
                    "batch": B, "tokens": int(lens.sum()), "block_size": w.block_size,
                    "us_per_call": round(us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -283,6 +293,9 @@ def prefill_workload(args):
     import workloads as W
 
     name = args.workload
+    f16 = name.endswith("_f16")  # the same batch on IEEE fp16 pools
+    if f16:
+        name = name[:-len("_f16")]
     if name == "llama3_8b_prefill":
         chunk = None
     elif name.startswith("llama3_8b_chunked_prefill_c"):
@@ -297,9 +310,10 @@ def prefill_workload(args):
     T, H_q, D = int(qs[-1]), w.num_q_heads, w.head_dim
     shape = (w.num_blocks, w.num_kv_heads, w.block_size, D)
     gen = torch.Generator(device=dev).manual_seed(w.seed)
-    kp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(args.layers)]
-    vp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(args.layers)]
-    q = torch.randn((T, H_q, D), generator=gen, device=dev).to(torch.bfloat16)
+    dt = torch.float16 if f16 else torch.bfloat16
+    kp = [torch.randn(shape, generator=gen, device=dev).to(dt) for _ in range(args.layers)]
+    vp = [torch.randn(shape, generator=gen, device=dev).to(dt) for _ in range(args.layers)]
+    q = torch.randn((T, H_q, D), generator=gen, device=dev).to(dt)
     outs = [torch.empty_like(q) for _ in range(args.layers)]
     td = torch.from_numpy(tables).to(dev)
     ld = torch.from_numpy(lens).to(dev)
@@ -309,14 +323,15 @@ def prefill_workload(args):
                       args.kernel_reps) / args.layers
     flops = prefill_flops(lens, nq, H_q, D)
     tfs = flops / (us * 1e-6) / 1e12
-    log(f"{name}: B={w.batch} query tokens={T} cache tokens={int(lens.sum())}: {us:.2f} us/call, "
-        f"{tfs:.1f} TFLOP/s")
+    log(f"{args.workload}: B={w.batch} query tokens={T} cache tokens={int(lens.sum())}: "
+        f"{us:.2f} us/call, {tfs:.1f} TFLOP/s")
     result = {
         "metric": PREFILL_METRIC, "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.kernel_reps * args.layers, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"{name}: pa_prefill alone, {args.layers} layer pools, graph replay; "
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if f16 else "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: pa_prefill alone, {args.layers} layer pools, "
+                               "graph replay; "
                                "32 Q / 8 KV heads, head 128, bs 16, bf16",
                    "batch": w.batch, "query_tokens": T, "cache_tokens": int(lens.sum()),
                    "query_tokens_per_seq": nq.tolist(), "us_per_call": round(us, 3)},
@@ -325,7 +340,7 @@ def prefill_workload(args):
                      "traffic": None, "kernel": "pa_prefill (one kernel), one layer",
                      "us_per_launch": round(us, 3), "algorithmic_flops_per_call": flops},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not f16:
         log("cpu baseline (oracle)...")
         result["cpu_baseline"] = cpu_baseline_prefill(w.seed, chunk, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -535,7 +550,7 @@ def main():
               "shards by sequence or KV head with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
-    if args.workload != "llama3_8b_decode":
+    if args.workload != "llama3_8b_decode":  # kernel legs on other workloads
         if args.layers == 32:
             args.layers = 2  # each of these batches is larger than the last-level cache
         if "prefill" in args.workload:

@@ -64,9 +64,14 @@ typedef int32_t pa_status;
 typedef int32_t pa_dtype;
 #define PA_F32 0
 #define PA_BF16 1
+#define PA_F16 2 /* IEEE binary16 */
 
 /* Shape of one KV pool pair.  Supported: block_size a power of two in
- * [1, 256]; head_dim 64 or 128; dtype PA_F32 or PA_BF16. */
+ * [1, 256]; head_dim 64 or 128; dtype PA_F32, PA_BF16 or PA_F16.  The two
+ * 16-bit formats halve every block against fp32 [P3 Trade-offs and edge
+ * cases, fourth point: narrower cache values shrink every block; P3 Step 1:
+ * 2-byte values]; attention computes in fp32 and rounds its probabilities
+ * and output to the pool's format. */
 typedef struct pa_cache_desc {
   int32_t num_blocks;
   int32_t block_size;
@@ -186,8 +191,9 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * p = L - n_b + i and, for every query head h (KV head h / G):
  *   out[query_start[b] + i][h] = sum_{t <= p} softmax(s)_t * V(b, t, kvh),
  *   s_t = scale * dot(q[query_start[b] + i][h], K(b, t, kvh)).
- * q, out:       device [num_query_tokens][num_q_heads][head_dim], bf16 (the
- *               pools must be bf16; PA_ERR_UNSUPPORTED otherwise).
+ * q, out:       device [num_query_tokens][num_q_heads][head_dim], the pool
+ *               dtype, which must be 16-bit (PA_BF16 or PA_F16;
+ *               PA_ERR_UNSUPPORTED for PA_F32).
  * query_start:  device int32 [num_seqs + 1], non-decreasing from 0 to
  *               num_query_tokens (values are clamped into that range; n_b is
  *               clamped to [0, L]; L to max_blocks_per_seq * block_size).

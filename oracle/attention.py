@@ -36,8 +36,13 @@ from scipy.special import softmax
 
 
 def widen(x, dtype: str):
-    """Stored values -> float64, exactly.  ``dtype`` is 'f32' or 'bf16'."""
+    """Stored values -> float64, exactly.  ``dtype`` is 'f32', 'bf16' or 'f16'
+    (IEEE binary16, held as uint16 bit patterns like bf16)."""
     x = np.asarray(x)
+    if dtype == "f16":
+        if x.dtype != np.uint16:
+            raise TypeError("f16 values are passed as uint16 bit patterns")
+        return x.view(np.float16).astype(np.float64)
     if dtype == "bf16":
         if x.dtype != np.uint16:
             raise TypeError("bf16 values are passed as uint16 bit patterns")

@@ -27,6 +27,7 @@ PA_ERR_UNSUPPORTED = 4
 PA_ERR_DEVICE = 5
 PA_F32 = 0
 PA_BF16 = 1
+PA_F16 = 2
 
 STATUS_NAMES = {PA_ERR_INVALID_ARGUMENT: "INVALID_ARGUMENT", PA_ERR_OUT_OF_BLOCKS: "OUT_OF_BLOCKS",
                 PA_ERR_UNKNOWN_SEQ: "UNKNOWN_SEQ", PA_ERR_UNSUPPORTED: "UNSUPPORTED",
@@ -135,6 +136,8 @@ def _dtype_code(t):
         return PA_F32
     if t.dtype == torch.bfloat16:
         return PA_BF16
+    if t.dtype == torch.float16:
+        return PA_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

@@ -31,21 +31,21 @@ struct KvPool {
   int32_t log2_bs;
 };
 
-template <bool BF16, int D>
+template <bool k16, int D>
 struct Geometry {
-  static constexpr int kElem = BF16 ? 2 : 4;
+  static constexpr int kElem = k16 ? 2 : 4;
   static constexpr int kRowBytes = D * kElem;
   static constexpr int kKPieces = kRowBytes / 64;     // 16-byte K pieces per lane per tile
   static constexpr int kVWords = kRowBytes / 16 / 4;  // 32-bit words of V per lane per token
   static constexpr int kCols = D / 16;                // output columns per lane
-  static constexpr int kQRegs = BF16 ? kKPieces : 1;  // query as bf16 MFMA operand
-  static constexpr int kQF32 = BF16 ? 1 : kKPieces * 4;
+  static constexpr int kQRegs = k16 ? kKPieces : 1;  // query as 16-bit MFMA operand
+  static constexpr int kQF32 = k16 ? 1 : kKPieces * 4;
   static_assert(kRowBytes % 64 == 0, "row must be a multiple of 64 bytes");
 };
 
-template <bool BF16, int D>
+template <bool k16, int D>
 struct TileRegs {
-  using Geo = Geometry<BF16, D>;
+  using Geo = Geometry<k16, D>;
   u32x4_t k[Geo::kKPieces];
   uint32_t v[4][Geo::kVWords];
 };
@@ -70,11 +70,11 @@ constexpr int32_t kRsrcWord3 = 0x00020000;
 // (`valid` false) gets a zero-length resource, so its loads return zeros
 // without touching memory.  Rows past the context length stay inside the
 // block and are masked when consumed.
-template <bool BF16, int D>
-__device__ __forceinline__ void issue_tile(TileRegs<BF16, D>& r, const KvPool& a,
+template <bool k16, int D>
+__device__ __forceinline__ void issue_tile(TileRegs<k16, D>& r, const KvPool& a,
                                            int32_t phys, int32_t t, int32_t kvh, int lane,
                                            bool valid) {
-  using Geo = Geometry<BF16, D>;
+  using Geo = Geometry<k16, D>;
   const int bs_log = a.log2_bs;
   const int32_t bs = 1 << bs_log;
   const int jr = lane >> 4, c16 = lane & 15;
@@ -122,11 +122,11 @@ __device__ __forceinline__ void issue_tile(TileRegs<BF16, D>& r, const KvPool& a
 // lane reads its own rows' blocks.  Rows past the context length L (and
 // padding tiles, whose index the caller clamps) read the last valid token
 // again.
-template <bool BF16, int D>
-__device__ __forceinline__ void issue_tile_small(TileRegs<BF16, D>& r, const KvPool& a,
+template <bool k16, int D>
+__device__ __forceinline__ void issue_tile_small(TileRegs<k16, D>& r, const KvPool& a,
                                                  int32_t phys_v, int32_t jl, int32_t t,
                                                  int32_t kvh, int32_t L, int nbt, int lane) {
-  using Geo = Geometry<BF16, D>;
+  using Geo = Geometry<k16, D>;
   const int bs_log = a.log2_bs;
   const int32_t bs = 1 << bs_log;
   const int jr = lane >> 4, c16 = lane & 15;
@@ -166,9 +166,9 @@ __device__ __forceinline__ void issue_tile_small(TileRegs<BF16, D>& r, const KvP
 // t0 = first token of the tile within its sequence, end = context length.
 
 
-// Per-wave state over one piece, bf16 pools (P*V by MFMA).
+// Per-wave state over one piece, 16-bit pools (P*V by MFMA).
 //  ref: lane 16j + g: reference max of head g (log2 units), equal in all rows.
-//  l:   lane 16j + c, register r: sum of the (bf16-rounded) weights of head
+//  l:   lane 16j + c, register r: sum of the (16-bit-rounded) weights of head
 //       4j + r, equal in every column c (an MFMA of P against ones).
 //  acc[blk]: lane 16j + c, register r: unnormalised output of head 4j + r at
 //       column (D/16)*c + blk.
@@ -187,7 +187,7 @@ struct MfmaState {
   }
 };
 
-// Consumes one tile (bf16): logits S = K q^T by MFMA (lane 16j + c holds
+// Consumes one tile (16-bit kind E): logits S = K q^T by MFMA (lane 16j + c holds
 // query row c, tokens 4j..4j+3); weights p = 2^(x - ref) against a reference
 // max that is raised (and the accumulators rescaled) only when a logit
 // exceeds it by more than 2^8, so the common tile needs no cross-lane
@@ -200,7 +200,7 @@ struct MfmaState {
 // kTail: key t of the tile is masked for the lane's query row when t > lim
 // (lim may differ per lane: a causal limit), and V rows at or past vend (the
 // tokens in the cache) are zeroed.
-template <int D, bool kTail>
+template <int E, int D, bool kTail>
 __device__ __forceinline__ void consume_tile_mfma_impl(MfmaState<D>& st,
                                                        const TileRegs<true, D>& r,
                                                        const u32x4_t* qf, float scale_log2,
@@ -211,9 +211,7 @@ __device__ __forceinline__ void consume_tile_mfma_impl(MfmaState<D>& st,
   const int jr = lane >> 4;
   floatx4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int p = 0; p < Geo::kKPieces; ++p)
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[p]),
-                                                __builtin_bit_cast(bf16x8_t, qf[p]), s, 0, 0, 0);
+  for (int p = 0; p < Geo::kKPieces; ++p) s = mfma_k32<E>(r.k[p], qf[p], s);
   float x[4];
   bool hi = false;
 #pragma unroll
@@ -237,11 +235,11 @@ __device__ __forceinline__ void consume_tile_mfma_impl(MfmaState<D>& st,
       for (int b = 0; b < kBlk; ++b) st.acc[b][q] *= fr;
     });
   }
-  const f32x2_t p01 = {__builtin_amdgcn_exp2f(x[0] - st.ref), __builtin_amdgcn_exp2f(x[1] - st.ref)};
-  const f32x2_t p23 = {__builtin_amdgcn_exp2f(x[2] - st.ref), __builtin_amdgcn_exp2f(x[3] - st.ref)};
-  const uint32_t a01 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t));
-  const uint32_t a23 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t));
-  const s16x4_t pa_ = __builtin_bit_cast(s16x4_t, (uint64_t)a01 | ((uint64_t)a23 << 32));
+  const uint32_t a01 = pack2<E>(__builtin_amdgcn_exp2f(x[0] - st.ref),
+                                 __builtin_amdgcn_exp2f(x[1] - st.ref));
+  const uint32_t a23 = pack2<E>(__builtin_amdgcn_exp2f(x[2] - st.ref),
+                                 __builtin_amdgcn_exp2f(x[3] - st.ref));
+  const uint64_t pa_ = (uint64_t)a01 | ((uint64_t)a23 << 32);
   uint32_t m01 = 0xFFFFFFFFu, m23 = 0xFFFFFFFFu;
   if constexpr (kTail) {
     const int32_t row0 = t0 + jr * 4;
@@ -258,11 +256,10 @@ __device__ __forceinline__ void consume_tile_mfma_impl(MfmaState<D>& st,
       v01 &= m01;
       v23 &= m23;
     }
-    const s16x4_t vb = __builtin_bit_cast(s16x4_t, (uint64_t)v01 | ((uint64_t)v23 << 32));
-    st.acc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_, vb, st.acc[b], 0, 0, 0);
+    st.acc[b] = mfma_k16<E>(pa_, (uint64_t)v01 | ((uint64_t)v23 << 32), st.acc[b]);
   }
-  const s16x4_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};  // bf16 1.0
-  st.l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_, ones, st.l, 0, 0, 0);
+  constexpr uint64_t ones = (uint64_t)kOnes2<E> | ((uint64_t)kOnes2<E> << 32);  // 1.0 x 4
+  st.l = mfma_k16<E>(pa_, ones, st.l);
 }
 
 }  // namespace pa

@@ -66,7 +66,6 @@
 
 namespace {
 
-using pa::bf16x2_t;
 using pa::bf16x8_t;
 using pa::f32x2_t;
 using pa::floatx4_t;
@@ -122,9 +121,9 @@ struct DecodeArgs {
   __device__ pa::KvPool pool() const { return {k_cache, v_cache, num_blocks, H_kv, log2_bs}; }
 };
 
-template <bool BF16, int D, int GP>
+template <bool k16, int D, int GP>
 struct WaveState {
-  using Geo = Geometry<BF16, D>;
+  using Geo = Geometry<k16, D>;
   float m;                  // lane 16j+g: running max of head g over row j (log2 units)
   float l;                  // lane 16j+g: running sum of exp2(x - m)
   float o[GP][Geo::kCols];  // lane 16j+c: unnormalised output, columns of chunk c
@@ -196,18 +195,16 @@ __device__ __forceinline__ void seg_advance(Seg& s, const int32_t* PB, const int
   s.L = uni(Ls[b]);
 }
 
-template <bool BF16, int D, int GP>
-__device__ __forceinline__ void consume_tile(WaveState<BF16, D, GP>& st,
-                                             const TileRegs<BF16, D>& r, const u32x4_t* qf,
+template <int E, int D, int GP>
+__device__ __forceinline__ void consume_tile(WaveState<(E != 0), D, GP>& st,
+                                             const TileRegs<(E != 0), D>& r, const u32x4_t* qf,
                                              const float* qf32, float scale_log2, int32_t t0,
                                              int32_t end, int lane) {
-  using Geo = Geometry<BF16, D>;
+  using Geo = Geometry<(E != 0), D>;
   floatx4_t s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (BF16) {
+  if constexpr (E != 0) {
 #pragma unroll
-    for (int p = 0; p < Geo::kKPieces; ++p)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[p]),
-                                                  __builtin_bit_cast(bf16x8_t, qf[p]), s, 0, 0, 0);
+    for (int p = 0; p < Geo::kKPieces; ++p) s = pa::mfma_k32<E>(r.k[p], qf[p], s);
   } else {
 #pragma unroll
     for (int p = 0; p < Geo::kKPieces; ++p) {
@@ -242,9 +239,9 @@ __device__ __forceinline__ void consume_tile(WaveState<BF16, D, GP>& st,
     const bool ok = !tail || (t0 + jr * 4 + q < end);
 #pragma unroll
     for (int w = 0; w < Geo::kVWords; ++w) {
-      if constexpr (BF16) {
-        vf[q][2 * w] = ok ? pa::bf16_lo(r.v[q][w]) : 0.f;
-        vf[q][2 * w + 1] = ok ? pa::bf16_hi(r.v[q][w]) : 0.f;
+      if constexpr (E != 0) {
+        vf[q][2 * w] = ok ? pa::lo16<E>(r.v[q][w]) : 0.f;
+        vf[q][2 * w + 1] = ok ? pa::hi16<E>(r.v[q][w]) : 0.f;
       } else {
         vf[q][w] = ok ? pa::as_float(r.v[q][w]) : 0.f;
       }
@@ -268,22 +265,22 @@ __device__ __forceinline__ void consume_tile(WaveState<BF16, D, GP>& st,
 
 // kSplit: take the unmasked variant for whole tiles (a uniform branch);
 // otherwise always mask (one code copy, for register-tight callers).
-template <int D, bool kSplit>
+template <int E, int D, bool kSplit>
 __device__ __forceinline__ void consume_tile_mfma(MfmaState<D>& st, const TileRegs<true, D>& r,
                                                   const u32x4_t* qf, float scale_log2,
                                                   int32_t t0, int32_t end, int lane) {
   if (kSplit && t0 + kTile <= end)
-    pa::consume_tile_mfma_impl<D, false>(st, r, qf, scale_log2, t0, end - 1, end, lane);
+    pa::consume_tile_mfma_impl<E, D, false>(st, r, qf, scale_log2, t0, end - 1, end, lane);
   else
-    pa::consume_tile_mfma_impl<D, true>(st, r, qf, scale_log2, t0, end - 1, end, lane);
+    pa::consume_tile_mfma_impl<E, D, true>(st, r, qf, scale_log2, t0, end - 1, end, lane);
 }
 
 // Loads the G query rows of segment (b, kvh) as the MFMA B operand (lane
 // 16j + g holds 16-byte pieces of head g; zero for g >= G).
-template <bool BF16, int D>
+template <bool k16, int D>
 __device__ __forceinline__ void load_q(const DecodeArgs& a, int32_t b, int32_t kvh, u32x4_t* qf,
                                        float* qf32, int lane) {
-  using Geo = Geometry<BF16, D>;
+  using Geo = Geometry<k16, D>;
   const int jr = lane >> 4, c16 = lane & 15;
   const bool live = c16 < a.G;
   const int64_t row = ((int64_t)b * a.H_kv + kvh) * a.G + (live ? c16 : 0);
@@ -292,7 +289,7 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int32_t b, int32_t k
   for (int p = 0; p < Geo::kKPieces; ++p) {
     u32x4_t x = *reinterpret_cast<const u32x4_t*>(qb + p * 64);
     if (!live) x = u32x4_t{0, 0, 0, 0};
-    if constexpr (BF16) {
+    if constexpr (k16) {
       qf[p] = x;
     } else {
 #pragma unroll
@@ -307,17 +304,18 @@ __device__ __forceinline__ int32_t share_of(int32_t f, int32_t T, int32_t W) {
   return static_cast<int32_t>((((int64_t)f + 1) * W - 1) / T);
 }
 
-template <bool BF16>
+template <int E>
 __device__ __forceinline__ void store_out(void* out, int64_t i, float x) {
-  if constexpr (BF16) reinterpret_cast<uint16_t*>(out)[i] = pa::f32_to_bf16_rne(x);
+  if constexpr (E != 0) reinterpret_cast<uint16_t*>(out)[i] = pa::round16<E>(x);
   else reinterpret_cast<float*>(out)[i] = x;
 }
 
-template <bool BF16, int D, int GP, int kNW, int NBUF, bool kSmall>
+template <int E, int D, int GP, int kNW, int NBUF, bool kSmall>
 __global__ void __launch_bounds__(kNW * kWave)
-__attribute__((amdgpu_waves_per_eu(kSmall ? ((BF16 || GP * D < 16 * 128) ? PA_DECODE_OCC : 1)
-                                          : (BF16 ? PA_DECODE_OCC_STREAM : 1))))
+__attribute__((amdgpu_waves_per_eu(kSmall ? (((E != 0) || GP * D < 16 * 128) ? PA_DECODE_OCC : 1)
+                                          : ((E != 0) ? PA_DECODE_OCC_STREAM : 1))))
 decode_kernel(DecodeArgs a) {
+  constexpr bool BF16 = E != 0;  // 16-bit pools (bf16 or fp16)
   using Geo = Geometry<BF16, D>;
   constexpr int kWG = kNW * kWave;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -366,7 +364,7 @@ decode_kernel(DecodeArgs a) {
   for (int32_t b = wg; b < B; b += nwg) {
     if (Ls[b] == 0) {
       for (int32_t e = tid; e < H_q * D; e += kWG)
-        store_out<BF16>(a.out, (int64_t)b * H_q * D + e, 0.f);
+        store_out<E>(a.out, (int64_t)b * H_q * D + e, 0.f);
       for (int32_t h = tid; h < H_kv; h += kWG) a.records[(b * H_kv + h) * kRecInts] = 0;
     }
   }
@@ -420,8 +418,7 @@ decode_kernel(DecodeArgs a) {
             uint32_t pk[kBlk / 2];
 #pragma unroll
             for (int i = 0; i < kBlk / 2; ++i) {
-              const f32x2_t pr = {st.acc[2 * i][q] * inv, st.acc[2 * i + 1][q] * inv};
-              pk[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+              pk[i] = pa::pack2<E>(st.acc[2 * i][q] * inv, st.acc[2 * i + 1][q] * inv);
             }
             char* dst = reinterpret_cast<char*>(a.out) +
                         ((((int64_t)s.b * H_kv + s.kvh) * G + g) * D + kBlk * c16) * 2;
@@ -454,7 +451,7 @@ decode_kernel(DecodeArgs a) {
           if (whole) {
             const int64_t base = (((int64_t)s.b * H_kv + s.kvh) * G + g) * D + c16 * Geo::kCols;
 #pragma unroll
-            for (int c = 0; c < Geo::kCols; ++c) store_out<BF16>(a.out, base + c, o[c] * inv);
+            for (int c = 0; c < Geo::kCols; ++c) store_out<E>(a.out, base + c, o[c] * inv);
           } else {
 #pragma unroll
             for (int c = 0; c < Geo::kCols; ++c) slot[g * D + c16 * Geo::kCols + c] = o[c];
@@ -584,8 +581,8 @@ decode_kernel(DecodeArgs a) {
           constexpr int u = decltype(U)::value;
           if (u < bt.nA) {
             const int32_t tok0 = kTile * (bt.fa + u - bt.A.S0);
-            if constexpr (BF16) consume_tile_mfma<D, true>(st, buf[u], qa, a.scale_log2, tok0, bt.A.L, lane);
-            else consume_tile(st, buf[u], qa, qa32, a.scale_log2, tok0, bt.A.L, lane);
+            if constexpr (BF16) consume_tile_mfma<E, D, true>(st, buf[u], qa, a.scale_log2, tok0, bt.A.L, lane);
+            else consume_tile<E, D, GP>(st, buf[u], qa, qa32, a.scale_log2, tok0, bt.A.L, lane);
           }
         });
         if (bt.endA) {
@@ -596,8 +593,8 @@ decode_kernel(DecodeArgs a) {
           constexpr int u = decltype(U)::value;
           if (u >= bt.nA && u < bt.n) {
             const int32_t tok0 = kTile * (bt.fa + u - bt.B.S0);
-            if constexpr (BF16) consume_tile_mfma<D, true>(st, buf[u], qb, a.scale_log2, tok0, bt.B.L, lane);
-            else consume_tile(st, buf[u], qb, qb32, a.scale_log2, tok0, bt.B.L, lane);
+            if constexpr (BF16) consume_tile_mfma<E, D, true>(st, buf[u], qb, a.scale_log2, tok0, bt.B.L, lane);
+            else consume_tile<E, D, GP>(st, buf[u], qb, qb32, a.scale_log2, tok0, bt.B.L, lane);
           }
         });
         if (bt.endB) {
@@ -621,8 +618,8 @@ decode_kernel(DecodeArgs a) {
         auto consume = [&](const TileRegs<BF16, D>& r, int32_t j) {
           const int32_t tok0 = kTile * (t0 + j);
           const int32_t end = j < n ? s.L : tok0;  // padding: every row masked
-          if constexpr (BF16) consume_tile_mfma<D, false>(st, r, qf, a.scale_log2, tok0, end, lane);
-          else consume_tile(st, r, qf, qf32, a.scale_log2, tok0, end, lane);
+          if constexpr (BF16) consume_tile_mfma<E, D, false>(st, r, qf, a.scale_log2, tok0, end, lane);
+          else consume_tile<E, D, GP>(st, r, qf, qf32, a.scale_log2, tok0, end, lane);
         };
         // Blocks smaller than a tile: block ids of a chunk of tiles in a
         // VGPR (one per lane), one chunk ahead.  Lanes past the piece repeat
@@ -674,7 +671,7 @@ decode_kernel(DecodeArgs a) {
 // head's row for the contributors congruent to t / (D/4); the slices'
 // (max, sum, output) are then combined through LDS, so the dependent-load
 // depth is n / (number of slices), not n.
-template <bool BF16, int D>
+template <int E, int D>
 __global__ void __launch_bounds__(kMergeWG)
 merge_kernel(DecodeArgs a) {
   constexpr int kCols = D / 4;
@@ -745,11 +742,9 @@ merge_kernel(DecodeArgs a) {
   }
   const float inv = 1.f / l;
   const int64_t base = (((int64_t)b * a.H_kv + kvh) * G + g) * D + 4 * col;
-  if constexpr (BF16) {
-    const f32x2_t lo = {o[0] * inv, o[1] * inv}, hi = {o[2] * inv, o[3] * inv};
+  if constexpr (E != 0) {
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + base) =
-        uint2{__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
-              __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t))};
+        uint2{pa::pack2<E>(o[0] * inv, o[1] * inv), pa::pack2<E>(o[2] * inv, o[3] * inv)};
   } else {
     *reinterpret_cast<floatx4_t*>(reinterpret_cast<float*>(a.out) + base) = o * inv;
   }
@@ -783,22 +778,22 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t H_q, int32_t B)
 
 // Waves per workgroup and tiles per batch.  Waves are independent, so the
 // workgroup size only sets how often the lengths prologue is repeated.
-template <bool BF16, int D, int GP>
+template <bool k16, int D, int GP>
 struct Config {
   static constexpr int kNW = PA_DECODE_NW;
   // fp32 pools with large query groups hold G*D/16 output floats per lane
   // in registers, which leaves room for one tile per batch only.
   static constexpr int NBUF =
-      BF16 ? (GP >= 8 ? 2 : PA_DECODE_NB_BF16) : (GP * D >= 8 * 64 ? 1 : 2);
+      k16 ? (GP >= 8 ? 2 : PA_DECODE_NB_BF16) : (GP * D >= 8 * 64 ? 1 : 2);
 };
 
 size_t lds_bytes(int nw, int32_t B) { return (size_t)(2 * B + 1 + nw) * sizeof(int32_t); }
 
-template <bool BF16, int D, int GP>
+template <int E, int D, int GP>
 pa_status launch(const DecodeArgs& a, hipStream_t s) {
-  using C = Config<BF16, D, GP>;
-  auto kern = a.log2_bs >= 4 ? decode_kernel<BF16, D, GP, C::kNW, C::NBUF, false>
-                             : decode_kernel<BF16, D, GP, C::kNW, C::NBUF, true>;
+  using C = Config<(E != 0), D, GP>;
+  auto kern = a.log2_bs >= 4 ? decode_kernel<E, D, GP, C::kNW, C::NBUF, false>
+                             : decode_kernel<E, D, GP, C::kNW, C::NBUF, true>;
   const size_t lds = lds_bytes(C::kNW, a.B);
   if (lds > kMaxLds)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: %d sequences need %zu bytes of LDS (> %zu)",
@@ -811,19 +806,19 @@ pa_status launch(const DecodeArgs& a, hipStream_t s) {
   }
   const int wgs = decode_wgs(C::kNW);
   hipLaunchKernelGGL(kern, dim3(wgs), dim3(C::kNW * kWave), lds, s, a);
-  hipLaunchKernelGGL((merge_kernel<BF16, D>), dim3(a.B * a.H_kv, a.G), dim3(kMergeWG), 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<E, D>), dim3(a.B * a.H_kv, a.G), dim3(kMergeWG), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_DEVICE, "pa_decode: %s", hipGetErrorString(e));
   return PA_OK;
 }
 
-template <bool BF16, int D>
+template <int E, int D>
 pa_status dispatch_g(const DecodeArgs& a, hipStream_t s) {
-  if (a.G <= 1) return launch<BF16, D, 1>(a, s);
-  if (a.G <= 2) return launch<BF16, D, 2>(a, s);
-  if (a.G <= 4) return launch<BF16, D, 4>(a, s);
-  if (a.G <= 8) return launch<BF16, D, 8>(a, s);
-  return launch<BF16, D, 16>(a, s);
+  if (a.G <= 1) return launch<E, D, 1>(a, s);
+  if (a.G <= 2) return launch<E, D, 2>(a, s);
+  if (a.G <= 4) return launch<E, D, 4>(a, s);
+  if (a.G <= 8) return launch<E, D, 8>(a, s);
+  return launch<E, D, 16>(a, s);
 }
 
 }  // namespace
@@ -913,11 +908,12 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   a.log2_bs = pa::ilog2_exact(block_size);
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = desc->dtype == PA_BF16;
-  if (bf16 && desc->head_dim == 128) return dispatch_g<true, 128>(a, s);
-  if (bf16) return dispatch_g<true, 64>(a, s);
-  if (desc->head_dim == 128) return dispatch_g<false, 128>(a, s);
-  return dispatch_g<false, 64>(a, s);
+  const bool d128 = desc->head_dim == 128;
+  switch (desc->dtype) {
+    case PA_BF16: return d128 ? dispatch_g<1, 128>(a, s) : dispatch_g<1, 64>(a, s);
+    case PA_F16: return d128 ? dispatch_g<2, 128>(a, s) : dispatch_g<2, 64>(a, s);
+    default: return d128 ? dispatch_g<0, 128>(a, s) : dispatch_g<0, 64>(a, s);
+  }
 }
 
 }  // extern "C"

@@ -50,6 +50,79 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// ---- 16-bit element kinds.  E is the pool's element kind: 0 = fp32,
+// 1 = bf16, 2 = fp16 (the pa_dtype codes).  The helpers below pick the MFMA
+// instruction, the packing and the rounding of a 16-bit kind; for E = 1
+// they are exactly the bf16 operations.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef short s16x4_v __attribute__((ext_vector_type(4)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// 16x16x32 MFMA: a, b hold 8 elements each (4 words).
+template <int E>
+__device__ __forceinline__ floatx4_t mfma_k32(u32x4_t a, u32x4_t b, floatx4_t c) {
+  static_assert(E == 1 || E == 2, "16-bit kinds only");
+  if constexpr (E == 2)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 16x16x16 MFMA: a, b hold 4 elements each (2 words, as one 64-bit value).
+template <int E>
+__device__ __forceinline__ floatx4_t mfma_k16(uint64_t a, uint64_t b, floatx4_t c) {
+  static_assert(E == 1 || E == 2, "16-bit kinds only");
+  if constexpr (E == 2)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_v, a),
+                                                     __builtin_bit_cast(s16x4_v, b), c, 0, 0, 0);
+}
+
+// Two fp32 values rounded (to nearest even) and packed, lo in bits 0..15.
+template <int E>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const f32x2_v v = {lo, hi};
+  if constexpr (E == 2) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
+}
+
+// The 16-bit halves of a packed word, widened exactly to fp32.
+template <int E>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (E == 2)
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
+  else return __builtin_bit_cast(float, w << 16);
+}
+template <int E>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (E == 2)
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+  else return __builtin_bit_cast(float, w & 0xFFFF0000u);
+}
+
+// fp32 -> the 16-bit kind, round to nearest even.
+template <int E>
+__device__ __forceinline__ uint16_t round16(float x) {
+  if constexpr (E == 2) return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  else {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+  }
+}
+
+// Two 1.0 values of the kind, packed.
+template <int E>
+constexpr uint32_t kOnes2 = E == 2 ? 0x3C003C00u : 0x3F803F80u;
+
 // Workgroup barrier that orders LDS only: global loads still in flight are
 // not drained (unlike __syncthreads(), a full workgroup fence).
 __device__ __forceinline__ void lds_barrier() {

@@ -13,7 +13,7 @@ pa_status fail(pa_status status, const char* fmt, ...) __attribute__((format(pri
 int ilog2_exact(int32_t x);
 
 // Bytes per stored value of a pool dtype.
-inline int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
+inline int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
 
 // Validates a pool descriptor against the supported set (see pa.h).
 pa_status check_desc(const pa_cache_desc* desc);

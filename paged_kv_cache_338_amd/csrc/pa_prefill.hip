@@ -28,8 +28,8 @@
 // as the contraction.  Only the tiles that cross a wave's first diagonal
 // mask anything; K/V rows past the cache length are loaded as zeros.
 //
-// The query rows need MFMA operands in bf16, so the call takes bf16 pools
-// only.
+// The query rows are MFMA operands in the pool's 16-bit format, so the call
+// takes bf16 or fp16 pools.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -42,8 +42,6 @@
 
 namespace {
 
-using pa::bf16x2_t;
-using pa::bf16x8_t;
 using pa::f32x2_t;
 using pa::floatx4_t;
 using pa::kWave;
@@ -102,7 +100,7 @@ __device__ __forceinline__ int32_t find_item_seq(const int32_t* P, int32_t B, in
   return lo;
 }
 
-template <int D, int GP, int R>
+template <int E, int D, int GP, int R>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kOcc, kOcc)))
 prefill_kernel(PrefillArgs a) {
   using Geo = TileGeo<D>;
@@ -267,8 +265,8 @@ prefill_kernel(PrefillArgs a) {
     for (int k = 0; k < kBlk; ++k) acc[r][k] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
   const float inv_scale = scale > 0.f ? 1.f / scale : 0.f;
-  const bf16x8_t ones = __builtin_bit_cast(
-      bf16x8_t, u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  constexpr uint32_t k1 = pa::kOnes2<E>;
+  const u32x4_t ones = {k1, k1, k1, k1};
 
   // Raw scores of a tile: s[kb][r], lane 16j + c, register q = key
   // t0 + 16 kb + 4j + q against row c of block r; masked keys are -inf.
@@ -295,9 +293,7 @@ prefill_kernel(PrefillArgs a) {
       for (int ds = 0; ds < kDS; ++ds) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
-          s[kb][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, kf[kb][ds]), __builtin_bit_cast(bf16x8_t, qf[r][ds]),
-              s[kb][r], 0, 0, 0);
+          s[kb][r] = pa::mfma_k32<E>(kf[kb][ds], qf[r][ds], s[kb][r]);
       }
     }
 #pragma unroll
@@ -365,15 +361,12 @@ prefill_kernel(PrefillArgs a) {
       const float nr = -ref[r];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const f32x2_t p01 = {__builtin_amdgcn_exp2f(fmaf(s[kb][r][0], scale, nr)),
-                             __builtin_amdgcn_exp2f(fmaf(s[kb][r][1], scale, nr))};
-        const f32x2_t p23 = {__builtin_amdgcn_exp2f(fmaf(s[kb][r][2], scale, nr)),
-                             __builtin_amdgcn_exp2f(fmaf(s[kb][r][3], scale, nr))};
-        pp[r][2 * kb] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p01, bf16x2_t));
-        pp[r][2 * kb + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p23, bf16x2_t));
+        pp[r][2 * kb] = pa::pack2<E>(__builtin_amdgcn_exp2f(fmaf(s[kb][r][0], scale, nr)),
+                                     __builtin_amdgcn_exp2f(fmaf(s[kb][r][1], scale, nr)));
+        pp[r][2 * kb + 1] = pa::pack2<E>(__builtin_amdgcn_exp2f(fmaf(s[kb][r][2], scale, nr)),
+                                         __builtin_amdgcn_exp2f(fmaf(s[kb][r][3], scale, nr)));
       }
-      l[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pp[r]), ones,
-                                                     l[r], 0, 0, 0);
+      l[r] = pa::mfma_k32<E>(pp[r], ones, l[r]);
     }
     // For column group blk the lane's operand is V[key][kBlk*c+blk] over
     // its 8 keys, in P's key order.
@@ -387,9 +380,7 @@ prefill_kernel(PrefillArgs a) {
                           __builtin_amdgcn_perm(vw[1][3][w], vw[1][2][w], sel)};
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        acc[r][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, pp[r]), __builtin_bit_cast(bf16x8_t, vb), acc[r][k],
-            0, 0, 0);
+        acc[r][k] = pa::mfma_k32<E>(pp[r], vb, acc[r][k]);
     }
   };
 
@@ -471,8 +462,7 @@ prefill_kernel(PrefillArgs a) {
         uint32_t pk[kBlk / 2];
 #pragma unroll
         for (int k = 0; k < kBlk / 2; ++k) {
-          const f32x2_t pr = {acc[r][2 * k][q] * inv, acc[r][2 * k + 1][q] * inv};
-          pk[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+          pk[k] = pa::pack2<E>(acc[r][2 * k][q] * inv, acc[r][2 * k + 1][q] * inv);
         }
         char* dst = reinterpret_cast<char*>(a.out) +
                     (((int64_t)(uni(QS[b]) + ti) * H_q + kvh * G + g) * D + kBlk * c16) * 2;
@@ -483,9 +473,9 @@ prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, int GP, int R>
+template <int E, int D, int GP, int R>
 pa_status launch_r(const PrefillArgs& a, int64_t items, hipStream_t s) {
-  auto kern = prefill_kernel<D, GP, R>;
+  auto kern = prefill_kernel<E, D, GP, R>;
   const size_t lds = (((size_t)(3 * a.B + 1 + kNW) * 4 + 15) & ~(size_t)15) +
                      2 * TileGeo<D>::kStage;
   if (lds > 64 * 1024) {
@@ -507,22 +497,22 @@ inline int64_t prefill_items(const PrefillArgs& a, int GP, int R) {
   return (((int64_t)a.T + QT - 1) / QT + a.B) * a.pool.H_kv;
 }
 
-template <int D, int GP>
+template <int E, int D, int GP>
 pa_status launch(const PrefillArgs& a, hipStream_t s) {
   const int64_t items1 = prefill_items(a, GP, 1), items2 = prefill_items(a, GP, 2);
   if (items1 >= (1ll << 31))  // the kernel numbers items in int32
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: too many query blocks");
-  if (items2 >= kMinItemsR2) return launch_r<D, GP, 2>(a, items2, s);
-  return launch_r<D, GP, 1>(a, items1, s);
+  if (items2 >= kMinItemsR2) return launch_r<E, D, GP, 2>(a, items2, s);
+  return launch_r<E, D, GP, 1>(a, items1, s);
 }
 
-template <int D>
+template <int E, int D>
 pa_status dispatch_g(const PrefillArgs& a, hipStream_t s) {
-  if (a.G <= 1) return launch<D, 1>(a, s);
-  if (a.G <= 2) return launch<D, 2>(a, s);
-  if (a.G <= 4) return launch<D, 4>(a, s);
-  if (a.G <= 8) return launch<D, 8>(a, s);
-  return launch<D, 16>(a, s);
+  if (a.G <= 1) return launch<E, D, 1>(a, s);
+  if (a.G <= 2) return launch<E, D, 2>(a, s);
+  if (a.G <= 4) return launch<E, D, 4>(a, s);
+  if (a.G <= 8) return launch<E, D, 8>(a, s);
+  return launch<E, D, 16>(a, s);
 }
 
 }  // namespace
@@ -536,8 +526,8 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
                      int32_t num_q_heads, const pa_cache_desc* desc, void* stream) {
   pa_status st = pa_supported(desc, num_q_heads);
   if (st != PA_OK) return st;
-  if (desc->dtype != PA_BF16)
-    return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: bf16 pools only");
+  if (desc->dtype != PA_BF16 && desc->dtype != PA_F16)
+    return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: 16-bit (bf16 or fp16) pools only");
   if (block_size != desc->block_size)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "block_size %d != desc->block_size %d", block_size,
                     desc->block_size);
@@ -572,8 +562,9 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
   a.G = num_q_heads / desc->num_kv_heads;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   hipStream_t s = (hipStream_t)stream;
-  if (desc->head_dim == 128) return dispatch_g<128>(a, s);
-  return dispatch_g<64>(a, s);
+  const bool d128 = desc->head_dim == 128;
+  if (desc->dtype == PA_F16) return d128 ? dispatch_g<2, 128>(a, s) : dispatch_g<2, 64>(a, s);
+  return d128 ? dispatch_g<1, 128>(a, s) : dispatch_g<1, 64>(a, s);
 }
 
 }  // extern "C"

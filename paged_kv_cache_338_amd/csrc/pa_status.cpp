@@ -40,8 +40,8 @@ pa_status check_desc(const pa_cache_desc* desc) {
                 desc->block_size);
   if (desc->head_dim != 64 && desc->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", desc->head_dim);
-  if (desc->dtype != PA_F32 && desc->dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "dtype %d not in {PA_F32, PA_BF16}", desc->dtype);
+  if (desc->dtype != PA_F32 && desc->dtype != PA_BF16 && desc->dtype != PA_F16)
+    return fail(PA_ERR_UNSUPPORTED, "dtype %d not in {PA_F32, PA_BF16, PA_F16}", desc->dtype);
   return PA_OK;
 }
 

@@ -37,7 +37,8 @@ def _pinned(a, dtype):
     return _gd().to_torch(a, dtype, "cpu").pin_memory()
 
 
-@pytest.mark.parametrize("dtype,shape", [("bf16", (40, 8, 16, 128)), ("f32", (12, 2, 4, 64))])
+@pytest.mark.parametrize("dtype,shape", [("bf16", (40, 8, 16, 128)), ("f32", (12, 2, 4, 64)),
+                                         ("f16", (12, 2, 8, 64))])
 @pytest.mark.parametrize("pairs_on", ["device", "pinned"])
 def test_swap_blocks_bit_exact_both_directions(dtype, shape, pairs_on):
     import torch
@@ -48,7 +49,7 @@ def test_swap_blocks_bit_exact_both_directions(dtype, shape, pairs_on):
     k, v = W._normal(rng, shape, dtype), W._normal(rng, shape, dtype)
     poison = W.POISON_BITS[dtype]
     hshape = (nh,) + shape[1:]
-    hk = np.full(hshape, poison, np.uint16 if dtype == "bf16" else np.uint32)
+    hk = np.full(hshape, poison, np.uint32 if dtype == "f32" else np.uint16)
     if dtype == "f32":
         hk = hk.view(np.float32)
     hv = hk.copy()

@@ -136,3 +136,17 @@ def test_paged_contiguous_brute_agree(seed, B, G, H_kv, D, bs, max_len, dtype):
     cont = oatt.contiguous_decode(q, ks, vs, scale, dtype)
     np.testing.assert_allclose(paged, brute, atol=1e-12, rtol=0)
     np.testing.assert_allclose(paged, cont, atol=1e-12, rtol=0)
+
+
+def test_f16_widening_and_rounding_pins():
+    """IEEE binary16 bit patterns widen to their exact values, and the input
+    generator rounds to nearest even (1/3 -> 0x3555, the float nearest)."""
+    import workloads as W
+    bits = np.array([0x3C00, 0xC000, 0x0001, 0x7BFF, 0x3555, 0x8000], np.uint16)
+    got = oatt.widen(bits, "f16")
+    assert got.tolist() == [1.0, -2.0, 2.0 ** -24, 65504.0, 1365 / 4096, -0.0]
+    assert W.round_to_f16_bits(np.float32([1 / 3, 1.0, 65504.0, 2.0 ** -25 * 3]))[:3].tolist() == \
+        [0x3555, 0x3C00, 0x7BFF]
+    assert W.round_to_f16_bits(np.float32([2.0 ** -25 * 3]))[0] == 0x0002  # 1.5 ulp -> even (2)
+    with pytest.raises(TypeError):
+        oatt.widen(np.zeros(2, np.float16), "f16")

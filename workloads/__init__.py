@@ -32,9 +32,9 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-POISON_BITS = {"f32": np.uint32(0x7FC00000), "bf16": np.uint16(0x7FC0)}
-STORAGE = {"f32": np.float32, "bf16": np.uint16}
-BYTES = {"f32": 4, "bf16": 2}
+POISON_BITS = {"f32": np.uint32(0x7FC00000), "bf16": np.uint16(0x7FC0), "f16": np.uint16(0x7E00)}
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16}
+BYTES = {"f32": 4, "bf16": 2, "f16": 2}
 
 
 def round_to_bf16_bits(x):
@@ -44,11 +44,18 @@ def round_to_bf16_bits(x):
     return (rounded >> np.uint32(16)).astype(np.uint16)
 
 
+def round_to_f16_bits(x):
+    """float32 -> IEEE binary16 bit patterns (uint16), round to nearest even."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def _normal(rng, shape, dtype, draw=True):
     if not draw:
         return None
     x = rng.standard_normal(size=shape, dtype=np.float32)
-    return round_to_bf16_bits(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return round_to_bf16_bits(x)
+    return round_to_f16_bits(x) if dtype == "f16" else x
 
 
 @dataclass
