@@ -53,6 +53,12 @@ constexpr int kThreads = kNW * kWave;
 constexpr int kMaxSeqs = 8192;  // query starts and lengths snapshot in LDS
 constexpr int kKT = 32;         // keys per LDS tile
 constexpr int kOcc = 2;         // waves per SIMD the registers are sized for
+#ifndef PA_PREFILL_PD1
+#define PA_PREFILL_PD1 4  // tiles of loads in flight with one row block per wave
+#endif
+#ifndef PA_PREFILL_PD2
+#define PA_PREFILL_PD2 2  // ... with two (its registers hold two)
+#endif
 // Row blocks per wave: 2 normally, 1 when that leaves too few workgroups
 // to fill the chip (measured on the Llama-3-8B shape: R = 2 is faster from
 // about two workgroups per CU up, R = 1 below).
@@ -211,13 +217,14 @@ prefill_kernel(PrefillArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.pool.k_cache) + col0 * 16;
   const char* vbase = reinterpret_cast<const char*>(a.pool.v_cache) + col0 * 16;
   const int32_t nb1 = a.pool.num_blocks - 1;
-  auto table_entry = [&](int32_t kt) -> int32_t {
+  auto table_entry = [&](int32_t kt) __attribute__((always_inline)) -> int32_t {
     const int32_t key = min(kt * kKT + my_row, L - 1);
     return trow[min(key >> log2_bs, a.max_blocks - 1)];
   };
   // Every lane loads (the row is clamped into the cache), so the number of
   // loads in flight is the same on every path; stash zeroes rows past it.
-  auto gather = [&](int32_t kt, int32_t tb, u32x4_t (&kr)[kLoads], u32x4_t (&vr)[kLoads]) {
+  auto gather = [&](int32_t kt, int32_t tb, u32x4_t (&kr)[kLoads],
+                    u32x4_t (&vr)[kLoads]) __attribute__((always_inline)) {
     const int32_t key = min(kt * kKT + my_row, L - 1);
     const uint32_t row = (uint32_t)(min(max(tb, 0), nb1) * rows_per_block + kv_row) +
                          (uint32_t)(key & bs_mask);
@@ -230,7 +237,7 @@ prefill_kernel(PrefillArgs a) {
   };
   const int lds_off = my_row * Geo::kRowLds + col0 * 16;
   auto stash = [&](int32_t kt, int stage, const u32x4_t (&kr)[kLoads],
-                   const u32x4_t (&vr)[kLoads]) {
+                   const u32x4_t (&vr)[kLoads]) __attribute__((always_inline)) {
     char* kl = tiles + stage * Geo::kStage + lds_off;
     if (kt * kKT + kKT > L) {  // uniform: the tile reaches past the cache
       const bool in = kt * kKT + my_row < L;
@@ -274,7 +281,7 @@ prefill_kernel(PrefillArgs a) {
   // their LDS latency overlaps the softmax.
   floatx4_t s[2][R];
   uint32_t vw[2][4][kBlk / 2];  // V rows 16 kb + 4j + q, columns kBlk*c ..
-  auto front = [&](int stage, int32_t t0, bool masked) -> bool {
+  auto front = [&](int stage, int32_t t0, bool masked) __attribute__((always_inline)) -> bool {
     const char* Kl = tiles + stage * Geo::kStage;
     const char* Vl = Kl + Geo::kMat;
     u32x4_t kf[2][kDS];
@@ -333,7 +340,7 @@ prefill_kernel(PrefillArgs a) {
   };
   // Raises the references to the tile's row maxima (where larger) and
   // rescales l and acc: the only place that touches them outside an MFMA.
-  auto rescale = [&]() {
+  auto rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float m = fmaxf(fmaxf(fmaxf(s[0][r][0], s[0][r][1]), fmaxf(s[0][r][2], s[0][r][3])),
@@ -354,7 +361,7 @@ prefill_kernel(PrefillArgs a) {
   };
   // p = 2^(score * scale - ref) as the 32-deep operand (the lane's keys
   // 4j..4j+3, then 16+4j..16+4j+3), l += P 1, O += P V.
-  auto back = [&]() {
+  auto back = [&]() __attribute__((always_inline)) {
     u32x4_t pp[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -384,65 +391,82 @@ prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- the key loop, two tiles of loads in flight: at tile kt the
-  // registers of set kt & 1 hold tile kt (stored to LDS stage kt & 1, then
-  // reloaded with tile kt + 2) and the other set holds tile kt + 1.  The
-  // table entries of a tile are read before the gather of the tile before
-  // it, so waiting for them never waits for that gather (loads complete in
+  // ---- the key loop, N tiles of loads in flight (N register sets): at tile
+  // kt, set kt % N holds tile kt (stored to LDS stage kt % 2, then reloaded
+  // with tile kt + N) and the other sets hold tiles kt + 1 .. kt + N - 1.
+  // The table entry of a tile is read before the gather of the tile before
+  // it, so waiting for it never waits for that gather (loads complete in
   // order).  A tile whose logits exceed a reference leaves the inner loop
   // (after its one barrier, like every tile) to be rescaled and finished
   // outside it, so the hot loop touches the accumulators only through MFMA.
+  constexpr int N = R == 1 ? PA_PREFILL_PD1 : PA_PREFILL_PD2;
+  static_assert(N >= 2 && N % 2 == 0, "an even number of register sets");
   int32_t tb[2];
-  u32x4_t kr[2][kLoads], vr[2][kLoads];
+  u32x4_t kr[N][kLoads], vr[N][kLoads];
   // Tiles past the last are gathered too (clamped, never used): the loads
   // are unconditional so that the waits stay exact.
-  tb[0] = table_entry(0);
-  tb[1] = table_entry(1);
-  gather(0, tb[0], kr[0], vr[0]);
-  tb[0] = table_entry(2);
-  gather(1, tb[1], kr[1], vr[1]);
+  {
+    int32_t cur = table_entry(0);
+    pa::static_for<0, N>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const int32_t next = table_entry(j + 1);
+      gather(j, cur, kr[j], vr[j]);
+      cur = next;
+    });
+    tb[0] = cur;  // tile N's entry
+  }
   // One tile: returns true when it must be rescaled (its scores in s).
-  auto step = [&](int32_t kt, auto kSet) -> bool {
-    constexpr int x = decltype(kSet)::value, y = 1 - x;
-    stash(kt, x, kr[x], vr[x]);
-    tb[y] = table_entry(kt + 3);
-    gather(kt + 2, tb[x], kr[x], vr[x]);
+  auto step = [&](int32_t kt, auto kSet) __attribute__((always_inline)) -> bool {
+    constexpr int x = decltype(kSet)::value, p = x & 1;
+    stash(kt, p, kr[x], vr[x]);
+    tb[1 - p] = table_entry(kt + N + 1);
+    gather(kt + N, tb[p], kr[x], vr[x]);
     pa::lds_barrier();
     const int32_t t0 = kt * kKT;
     if (wave_live && t0 <= wp_max) {
-      if (front(x, t0, t0 + kKT - 1 > wp_min)) return true;
+      if (front(p, t0, t0 + kKT - 1 > wp_min)) return true;
       back();
     }
     return false;
   };
-  // Tiles go in pairs (set 0, set 1), so the two register sets keep their
-  // registers across iterations; the count is rounded up to even (a spare
-  // last tile computes nothing), and every wave passes exactly one barrier
-  // per tile on every path.
-  const int32_t nt2 = (ntiles + 1) & ~1;
-  const auto set0 = std::integral_constant<int, 0>{};
-  const auto set1 = std::integral_constant<int, 1>{};
+  // Tile kt with its set chosen at run time (only after a rescale).
+  auto step_any = [&](int32_t kt) __attribute__((always_inline)) -> bool {
+    bool r = false;
+    pa::static_for<0, N>([&](auto X) {
+      if (kt % N == decltype(X)::value) r = step(kt, X);
+    });
+    return r;
+  };
+  // Tiles go in groups of N (sets 0 .. N-1), so the register sets keep
+  // their registers across iterations; the count is rounded up to a
+  // multiple of N (spare last tiles compute nothing), and every wave passes
+  // exactly one barrier per tile on every path.
+  const int32_t ntot = (ntiles + N - 1) / N * N;
   int32_t kt = 0;
   while (true) {
-    int brk = -1;  // the set of the tile to rescale, if any
-    if ((kt & 1) && kt < nt2) {  // back from a rescale at an even tile
-      if (step(kt, set1)) brk = 1;
-      else ++kt;
+    bool brk = false;
+    while (kt % N != 0 && kt < ntot) {  // back from a rescale: realign
+      if (step_any(kt)) {
+        brk = true;
+        break;
+      }
+      ++kt;
     }
-    if (brk < 0) {
-      for (; kt < nt2; kt += 2) {
-        if (step(kt, set0)) {
-          brk = 0;
-          break;
-        }
-        if (step(kt + 1, set1)) {
-          brk = 1;
-          ++kt;
+    if (!brk) {
+      for (; kt < ntot; kt += N) {
+        int u = -1;
+        pa::static_for<0, N>([&](auto U) {
+          constexpr int x = decltype(U)::value;
+          if (u < 0 && step(kt + x, U)) u = x;
+        });
+        if (u >= 0) {
+          kt += u;
+          brk = true;
           break;
         }
       }
     }
-    if (brk < 0) break;
+    if (!brk) break;
     rescale();
     back();
     ++kt;
