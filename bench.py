@@ -19,12 +19,16 @@ Lengths grow by one token per step, as in real decoding; the KV bytes of
 every step are counted exactly.
 
 Reported: value = KV bytes read by pa_decode per second over the timed steps
-(GB/s, whole step, all host work included).  roofline: pa_decode alone,
-timed with HIP events around back-to-back launches (a replayed graph of the
-32 layers' calls) at the batch's exact lengths, against the 8 TB/s HBM
-peak; one launch is the whole call, its two kernels included.  cpu_baseline:
-the CPU oracle's paged decode on the same batch (one layer), timed on this
-host.
+(GB/s, whole step, all host work included; 10 warm-up and 100 timed steps by
+default, with the median and p10/p90 of the per-step times).  roofline:
+pa_decode alone, timed with HIP events around back-to-back launches (100
+replays of a graph of the 32 layers' calls) at the batch's exact lengths,
+against the 8 TB/s HBM peak; one launch is the whole call, its two kernels
+included.  Beside it: the same calls on one pool (labelled MALL-warm: most
+of that pool then sits in the last-level cache) and the bandwidth of a plain
+1 GiB device copy on the same GPU.  cpu_baseline: the CPU oracle's paged
+decode on the same batch (one layer), timed on this host's cores, plus
+one-thread passes of this batch and of the tiny reference batch.
 """
 
 from __future__ import annotations
@@ -53,11 +57,11 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--layers", type=int, default=32)
-    p.add_argument("--kernel-reps", type=int, default=10,
-                   help="passes over the layer pools for the pa_decode roofline timing")
+    p.add_argument("--kernel-reps", type=int, default=100,
+                   help="graph replays (passes over the layer pools) for the kernel timing")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -121,15 +125,11 @@ def measured_traffic():
     return int(fields["traffic_bytes_per_call"])
 
 
-def cpu_baseline(w, seconds):
-    """The oracle (NumPy fp64) on one layer of the same batch."""
-    from threadpoolctl import threadpool_limits
-
+def oracle_decode_inputs(w):
+    """The oracle's pools, tables and lengths after the workload's script."""
     from oracle import allocator as oa
-    from oracle import attention as oatt
     from oracle import cache_ops as oc
 
-    cores = len(os.sched_getaffinity(0))
     alloc = oa.BlockAllocator(w.num_blocks, w.block_size, w.free_order)
     kc, vc = w.empty_pool(), w.empty_pool()
     for op in w.script:
@@ -140,22 +140,82 @@ def cpu_baseline(w, seconds):
             oc.cache_append(kc, vc, w.k_rows[op[3]], w.v_rows[op[3]], slots, w.block_size)
     maxb = max(len(alloc.seq_block_table(s)) for s in w.seq_ids)
     rows, lens = alloc.block_tables(w.seq_ids, maxb)
-    tables = np.array(rows, np.int32)
-    lens = np.array(lens, np.int32)
+    return kc, vc, np.array(rows, np.int32), np.array(lens, np.int32)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_oracle_decode(w, inputs, seconds, threads):
+    """Repeats the oracle's paged decode of one layer for about `seconds`
+    with `threads` BLAS/OpenMP threads: (passes, elapsed seconds)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oatt
+
+    kc, vc, tables, lens = inputs
     runs, t0 = 0, time.perf_counter()
-    with threadpool_limits(limits=cores):
+    with threadpool_limits(limits=threads):
         while True:
             oatt.paged_decode(w.q, kc, vc, tables, lens, w.block_size, w.scale, w.dtype)
             runs += 1
             el = time.perf_counter() - t0
             if el >= seconds:
-                break
+                return runs, el
+
+
+def cpu_baseline(w, seconds):
+    """The oracle (NumPy fp64) on one layer of the same batch, on every core
+    this process may use; plus one-thread passes of the same batch and of
+    the tiny reference batch."""
+    import workloads as W
+
+    cores = len(os.sched_getaffinity(0))
+    inputs = oracle_decode_inputs(w)
+    ntok = int(inputs[3].sum())
+    runs, el = time_oracle_decode(w, inputs, seconds, cores)
     per = el / runs
-    gbs = int(lens.sum()) * kv_bytes_per_token(w) / per / 1e9
+    gbs = ntok * kv_bytes_per_token(w) / per / 1e9
+    one = {}
+    for name, ww, inp, secs in (("llama3_8b_batch8", w, inputs, 2.0),
+                                ("tiny_ref", W.tiny_ref(), None, 1.0)):
+        inp = inp if inp is not None else oracle_decode_inputs(ww)
+        r1, e1 = time_oracle_decode(ww, inp, secs, 1)
+        one[name] = {"us_per_layer": round(e1 / r1 * 1e6, 1), "passes": r1,
+                     "GB/s": round(int(inp[3].sum()) * kv_bytes_per_token(ww) / (e1 / r1) / 1e9, 4)}
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "us_per_layer": round(per * 1e6, 1),
-            "sample": f"{runs} full passes of one layer of the batch ({int(lens.sum())} tokens) "
+            "us_per_layer": round(per * 1e6, 1), "cpu_model": cpu_model(),
+            "one_thread": one,
+            "sample": f"{runs} full passes of one layer of the batch ({ntok} tokens) "
                       f"in {el:.1f} s, NumPy fp64 paged decode incl. bf16 widening"}
+
+
+def copy_bandwidth(dev, nbytes=1 << 30, reps=5):
+    """A 1 GiB device-to-device copy (torch copy_), timed with HIP events:
+    the bandwidth a plain copy reaches on this GPU, beside the decode's."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del src, dst
+    return {"bytes": nbytes, "us": round(us, 1), "read_GBps": round(nbytes / us / 1e3, 1),
+            "read_plus_write_GBps": round(2 * nbytes / us / 1e3, 1)}
 
 
 def replay_timed(make_calls, reps):
@@ -632,19 +692,33 @@ def main():
 
     run_dec = captured(lambda: [pa.prepare_decode(q, kpool[l], vpool[l], tables_d, lens_d, bs,
                                                   w.scale, outs[l], ws) for l in range(nl)])
-    run_dec()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.kernel_reps):
-        run_dec()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    def timed_replays(run):
+        """Microseconds per call: the mean over all replays, and the
+        per-replay means (one HIP event between consecutive replays)."""
+        run()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_reps + 1)]
+        evs[0].record(stream)
+        for i in range(args.kernel_reps):
+            run()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.kernel_reps)])
+        return evs[0].elapsed_time(evs[-1]) * 1e3 / (args.kernel_reps * nl), per * 1e3 / nl
+
+    us_launch, per_rep = timed_replays(run_dec)
+    p10, p50, p90 = (float(x) for x in np.percentile(per_rep, [10, 50, 90]))
     launches = args.kernel_reps * nl
-    us_launch = e0.elapsed_time(e1) * 1e3 / launches
     kv_launch = int(lens_np.sum()) * kv_bytes_per_token(w)
     achieved = kv_launch / (us_launch * 1e-6) / 1e9
-    log(f"pa_decode: {us_launch:.2f} us/launch, {achieved:.0f} GB/s over {launches} launches")
+    log(f"pa_decode: {us_launch:.2f} us/launch (median {p50:.2f}, p10 {p10:.2f}, p90 {p90:.2f}), "
+        f"{achieved:.0f} GB/s over {launches} launches")
+    # The same calls all on layer 0's pools: the 268 MB pair then stays in
+    # the 256 MB last-level cache in large part (labelled MALL-warm).
+    us_warm, _ = timed_replays(captured(
+        lambda: [pa.prepare_decode(q, kpool[0], vpool[0], tables_d, lens_d, bs, w.scale,
+                                   outs[l], ws) for l in range(nl)]))
+    log(f"pa_decode, one pool (MALL-warm): {us_warm:.2f} us/launch")
 
     # ---- whole decode steps
     new_k = to_dev(w.notes["new_k"], w.dtype, dev)
@@ -700,17 +774,20 @@ def main():
     torch.cuda.synchronize()
     kv_read.clear()
     t_start = time.perf_counter()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record(stream)
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    sev[0].record(stream)
     for i in range(args.warmup, total_steps):
         step(i)
-    s1.record(stream)
+        sev[i - args.warmup + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    gpu_ms = s0.elapsed_time(s1)
+    gpu_ms = sev[0].elapsed_time(sev[-1])
     ms_step = max(gpu_ms, wall * 1e3) / args.steps
+    step_ms = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)])
+    sp10, sp50, sp90 = (float(x) for x in np.percentile(step_ms, [10, 50, 90]))
     value = sum(kv_read) / (ms_step * args.steps * 1e-3) / 1e9
-    log(f"steps: {ms_step:.3f} ms/step ({ms_step * 1e3 / nl:.2f} us/layer), {value:.0f} GB/s")
+    log(f"steps: {ms_step:.3f} ms/step ({ms_step * 1e3 / nl:.2f} us/layer; median {sp50:.3f}, "
+        f"p10 {sp10:.3f}, p90 {sp90:.3f} ms), {value:.0f} GB/s")
 
     mode = "eager launches" if args.eager else "HIP graph replay of the layer loop"
     result = {
@@ -724,7 +801,9 @@ def main():
                                "per layer",
                    "batch": B, "context_lens_at_first_step": (L0 + args.warmup + 1).tolist(),
                    "tokens_added_per_step": B, "layers": nl,
-                   "us_per_layer": round(ms_step * 1e3 / nl, 3)},
+                   "us_per_layer": round(ms_step * 1e3 / nl, 3),
+                   "step_ms_median": round(sp50, 4), "step_ms_p10": round(sp10, 4),
+                   "step_ms_p90": round(sp90, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
@@ -734,8 +813,17 @@ def main():
                      "kernel": "pa_decode (split + merge kernels), one layer, "
                                f"{int(lens_np.sum())} tokens x 4096 B",
                      "us_per_launch": round(us_launch, 3),
+                     "us_per_launch_median": round(p50, 3), "us_per_launch_p10": round(p10, 3),
+                     "us_per_launch_p90": round(p90, 3),
+                     "timing": f"{args.kernel_reps} replays of a graph of {nl} pa_decode calls, "
+                               f"one per layer pool; mean over all {launches} calls, median and "
+                               "p10/p90 of the per-replay means",
+                     "mall_warm_us_per_launch": round(us_warm, 3),
                      "algorithmic_bytes_per_call": kv_launch},
     }
+    cb = copy_bandwidth(dev)
+    result["roofline"]["copy_1gib"] = cb
+    log(f"1 GiB device copy: {cb['read_plus_write_GBps']:.0f} GB/s read + write")
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
