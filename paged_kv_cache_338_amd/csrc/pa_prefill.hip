@@ -63,6 +63,16 @@ constexpr int kOcc = 2;         // waves per SIMD the registers are sized for
 // to fill the chip (measured on the Llama-3-8B shape: R = 2 is faster from
 // about two workgroups per CU up, R = 1 below).
 constexpr int64_t kMinItemsR2 = 512;
+// Up to this many sequences, items are taken in the order of the sequences'
+// lengths, longest first (each workgroup ranks the lengths in its prologue);
+// beyond it, in batch order.
+constexpr int kSortMax = 256;
+static_assert(kSortMax <= kNW * kWave, "one sequence per thread while ranking");
+
+// Bytes of the LDS header (per-sequence snapshot) in front of the K/V tiles.
+__host__ __device__ constexpr int32_t header_bytes(int32_t B) {
+  return ((3 * B + 1 + kNW + (B <= kSortMax ? B : 0)) * 4 + 15) & ~15;
+}
 
 struct PrefillArgs {
   const void* q;            // [T][H_q][D]
@@ -94,7 +104,7 @@ struct TileGeo {
   static_assert(kLoads >= 1 && kKT * kPPR % kThreads == 0, "tile must split over the threads");
 };
 
-// Largest b in [0, B) with P[b] * H <= f (P: exclusive prefix sums in LDS).
+// Largest r in [0, B) with P[r] * H <= f (P: exclusive prefix sums in LDS).
 __device__ __forceinline__ int32_t find_item_seq(const int32_t* P, int32_t B, int32_t H,
                                                  int32_t f) {
   int32_t lo = 0, hi = B - 1;
@@ -121,27 +131,49 @@ prefill_kernel(PrefillArgs a) {
   const int log2_bs = a.pool.log2_bs;
   const int32_t len_cap = a.max_blocks << log2_bs;
 
-  // LDS: per sequence the query start, the number of query tokens n_b
-  // (clamped to [0, L_b]) and the exclusive prefix sums of its query
-  // blocks; then the two K/V tile stages.
+  // LDS: per sequence the query start and the number of query tokens n_b
+  // (clamped to [0, L_b]); the exclusive prefix sums of query blocks in
+  // processing order; for short batches the processing order itself (ORD:
+  // rank -> sequence, longest sequence first, so that the items that walk
+  // the most key tiles start first and the grid ends on short ones); then
+  // the two K/V tile stages.
+  const bool sorted = B <= kSortMax;
   int32_t* QS = reinterpret_cast<int32_t*>(smem);  // [B]
   int32_t* NQ = QS + B;                            // [B]
   int32_t* PQ = NQ + B;                            // [B + 1]
   int32_t* misc = PQ + B + 1;                      // [kNW]
-  char* tiles = smem + (((3 * B + 1 + kNW) * 4 + 15) & ~15);
+  int32_t* ORD = misc + kNW;                       // [B] when sorted
+  char* tiles = smem + header_bytes(B);
+  for (int32_t b = tid; b < B; b += kThreads) {
+    const int32_t q0 = min(max(a.qstart[b], 0), a.T);
+    const int32_t q1 = min(max(a.qstart[b + 1], q0), a.T);
+    const int32_t L = min(max(a.lens[b], 0), len_cap);
+    const int32_t n = min(q1 - q0, L);
+    QS[b] = q0;
+    NQ[b] = n;
+    PQ[b] = n > 0 ? L : -1;  // ranking key, replaced by the prefix sums below
+  }
+  __syncthreads();
+  if (sorted) {
+    // The last query token of a sequence attends to all of its L keys, so
+    // its first item walks ceil(L / 32) tiles: rank by L, ties by index.
+    int32_t rank = 0;
+    if (tid < B) {
+      const int32_t key = PQ[tid];
+      for (int32_t j = 0; j < B; ++j) {
+        const int32_t kj = PQ[j];
+        rank += (kj > key || (kj == key && j < tid)) ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    if (tid < B) ORD[rank] = tid;
+    __syncthreads();
+  }
   int32_t carry = 0;
   for (int32_t c = 0; c < B; c += kThreads) {
-    const int32_t b = c + tid;
+    const int32_t r = c + tid;
     int32_t nt = 0;
-    if (b < B) {
-      const int32_t q0 = min(max(a.qstart[b], 0), a.T);
-      const int32_t q1 = min(max(a.qstart[b + 1], q0), a.T);
-      const int32_t L = min(max(a.lens[b], 0), len_cap);
-      const int32_t n = min(q1 - q0, L);
-      QS[b] = q0;
-      NQ[b] = n;
-      nt = (n + QT - 1) / QT;
-    }
+    if (r < B) nt = (NQ[sorted ? ORD[r] : r] + QT - 1) / QT;
     const int32_t incl = pa::wave_incl_scan(nt);
     if (lane == kWave - 1) misc[v] = incl;
     __syncthreads();
@@ -152,19 +184,21 @@ prefill_kernel(PrefillArgs a) {
       pre += u < v ? x : 0;
       tot += x;
     }
-    if (b < B) PQ[b] = pre + incl - nt;
+    if (r < B) PQ[r] = pre + incl - nt;
     carry += tot;
     __syncthreads();
   }
   if (tid == 0) PQ[B] = carry;
   __syncthreads();
 
-  // ---- this workgroup's item: (b, kvh, query block qb), longest first
+  // ---- this workgroup's item: (b, kvh, query block qb); sequences in
+  // processing order, each one's query blocks longest first
   const int32_t items = uni(PQ[B]) * H_kv;
   const int32_t f = blockIdx.x;
   if (f >= items) return;  // the whole workgroup
-  const int32_t b = uni(find_item_seq(PQ, B, H_kv, f));
-  const int32_t local = f - uni(PQ[b]) * H_kv;
+  const int32_t rk = uni(find_item_seq(PQ, B, H_kv, f));
+  const int32_t b = sorted ? uni(ORD[rk]) : rk;
+  const int32_t local = f - uni(PQ[rk]) * H_kv;
   const int32_t kvh = local % H_kv;
   const int32_t nq = uni(NQ[b]);
   const int32_t qb = (nq + QT - 1) / QT - 1 - local / H_kv;
@@ -500,8 +534,7 @@ prefill_kernel(PrefillArgs a) {
 template <int E, int D, int GP, int R>
 pa_status launch_r(const PrefillArgs& a, int64_t items, hipStream_t s) {
   auto kern = prefill_kernel<E, D, GP, R>;
-  const size_t lds = (((size_t)(3 * a.B + 1 + kNW) * 4 + 15) & ~(size_t)15) +
-                     2 * TileGeo<D>::kStage;
+  const size_t lds = (size_t)header_bytes(a.B) + 2 * TileGeo<D>::kStage;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -147,6 +147,45 @@ def test_physical_relabelling_is_bit_identical():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("R2", [False, True], ids=["one_row_block", "two_row_blocks"])
+def test_sequence_order_is_bit_identical(R2):
+    """Items are taken longest sequence first (ties by batch index), so the
+    workgroup that computes a sequence depends on the whole batch.  Each
+    sequence's output must not: permuting the batch (tables, lengths, query
+    rows) permutes the outputs bit for bit.  The batch has equal lengths,
+    sequences without queries, and enough query blocks in the second case
+    for two row blocks per wave."""
+    if R2:
+        lengths = [256, 250, 256, 241, 256, 256, 199, 256, 60]
+        nq = [256, 250, 256, 241, 256, 256, 199, 256, 0]
+        G, H_kv = 4, 8
+    else:
+        lengths = [40, 300, 40, 7, 129, 1, 300, 64, 33, 5]
+        nq = [40, 120, 0, 7, 129, 1, 77, 64, 16, 0]
+        G, H_kv = 4, 2
+    q, k, v, t, lens, qs, bs = _case(61 + R2, lengths, nq, G=G, H_kv=H_kv, D=128)
+    a = _compare(q, k, v, t, lens, qs, bs, 1.0 / np.sqrt(128))
+    pi = np.random.default_rng(62).permutation(len(lengths))  # new batch slot i <- old pi[i]
+    nq2 = [nq[j] for j in pi]
+    qs2 = np.concatenate([[0], np.cumsum(nq2)]).astype(np.int32)
+    q2 = np.concatenate([q[qs[j]:qs[j + 1]] for j in pi])
+    b = _run(q2, k, v, np.ascontiguousarray(t[pi]), np.ascontiguousarray(lens[pi]), qs2, bs,
+             1.0 / np.sqrt(128))
+    for i, j in enumerate(pi):
+        assert np.array_equal(b[qs2[i]:qs2[i + 1]], a[qs[j]:qs[j + 1]]), (i, j)
+
+
+@pytest.mark.parametrize("B", [256, 257])
+def test_batches_at_the_ranking_limit(B):
+    """Up to 256 sequences the workgroups rank the lengths (longest first);
+    from 257 on they take the batch order: both sides of the limit against
+    the oracle."""
+    rng = np.random.default_rng(B)
+    lengths = [int(x) for x in rng.integers(1, 41, B)]
+    nq = [int(min(L, x)) for L, x in zip(lengths, rng.integers(0, 41, B))]
+    _check(B + 5, lengths, nq, G=4, H_kv=1, D=64, bs=16, spare=0)
+
+
 def test_rejects_f32_pools_and_bad_arguments():
     import torch
     import paged_kv_cache_338_amd as pa
