@@ -73,7 +73,9 @@ def parse():
                         "alone on that workload's batch (kernel leg only); llama3_8b_prefill, "
                         "llama3_8b_chunked_prefill_cN: pa_prefill alone on the worked batch; "
                         "swap_llama3_8b: pa_swap_blocks out to pinned host memory and back; "
-                        "prefix_cache_p2056: prefill with and without the prefix cache; a _f16 "
+                        "prefix_cache_p2056: prefill with and without the prefix cache; cache_ops: "
+                        "slot reservation, pa_copy_blocks, pa_cache_append and the metadata "
+                        "upload, each beside the oracle; a _f16 "
                         "suffix (llama3_8b_decode_f16, llama3_8b_prefill_f16, ...) runs a "
                         "decode or prefill leg on fp16 pools")
     p.add_argument("--eager", action="store_true",
@@ -320,6 +322,210 @@ def other_workload(args):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "algorithmic_bytes_per_call": kv}}), flush=True)
+
+
+CACHE_OPS_METRIC = ("paged KV cache maintenance on the pages' workloads: slot reservation (host), "
+                    "pa_copy_blocks, pa_cache_append, metadata upload")
+
+
+def cache_ops_workload(args):
+    """The steps around the decode kernel, each on the workload where the
+    pages put it, each timed beside the oracle doing the same on the host:
+
+    * llama3_8b (the worked batch): one decode step's reservation of one
+      token per sequence and the append of those 8 tokens;
+    * prefix_sharing_p2056: the first call after the forks reserves every
+      sequence's suffix plus one token (32,267 tokens), which copies the
+      shared, half-filled tail block for 127 of the 128 sequences; then
+      pa_copy_blocks of those 127 pairs and the append of the 32,267 tokens;
+    * serving_batch: the reservation and append of one token for each of
+      256 sequences, and the upload of the tables, lengths and slot mapping
+      from pinned host memory.
+
+    Device calls are captured in a graph over args.layers layer pools (32 by
+    default, a different pool each call) and replayed args.kernel_reps times; copies
+    and appends rewrite the same values, so every replay does the same
+    work.  Bytes: a copy reads and writes its whole blocks; an append reads
+    the tokens' K/V rows and writes them into the pool."""
+    import torch
+
+    import paged_kv_cache_338_amd as pa
+    import workloads as W
+    from oracle import allocator as oa
+    from oracle import cache_ops as oc
+
+    dev = "cuda:0"
+    layers = args.layers
+
+    def split_script(w):
+        """The script up to its last reservation, and that reservation."""
+        last = max(i for i, op in enumerate(w.script) if op[0] == "reserve")
+        return w.script[:last], w.script[last]
+
+    def replay(alloc, ops, fork, reserve):
+        for op in ops:
+            if op[0] == "create":
+                alloc.seq_create(op[1])
+            elif op[0] == "fork":
+                fork(op[1], op[2])
+            else:
+                reserve(op[1], op[2])
+
+    def host_reserve(w, reps):
+        """Microseconds of the last reservation: C++ allocator and oracle,
+        each replayed from a fresh allocator before every timed call."""
+        head, (_, sids, ns, _) = split_script(w)
+        cap = len(sids)
+        times = {"cpp": [], "oracle": []}
+        slots = pairs = None
+        for _ in range(reps):
+            a = pa.Allocator(w.num_blocks, w.block_size, w.free_order)
+            replay(a, head, a.seq_fork, lambda s, n: a.seq_reserve(s, n, cow_cap=len(s)))
+            t0 = time.perf_counter()
+            slots, pairs = a.seq_reserve(sids, ns, cow_cap=cap)
+            times["cpp"].append(time.perf_counter() - t0)
+            a.close()
+            o = oa.BlockAllocator(w.num_blocks, w.block_size, w.free_order)
+            replay(o, head, o.seq_fork, o.seq_reserve)
+            t0 = time.perf_counter()
+            oslots, opairs = o.seq_reserve(sids, ns)
+            times["oracle"].append(time.perf_counter() - t0)
+        assert np.array_equal(np.asarray(slots), np.asarray(oslots, np.int64))
+        assert np.array_equal(np.asarray(pairs).reshape(-1, 2), np.asarray(opairs, np.int64).reshape(-1, 2))
+        med = {k: float(np.median(v)) * 1e6 for k, v in times.items()}
+        return np.asarray(slots, np.int64), np.asarray(pairs, np.int32).reshape(-1, 2), med
+
+    def device_pools(w):
+        shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        gen = torch.Generator(device=dev).manual_seed(w.seed)
+        kp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(layers)]
+        vp = [torch.randn(shape, generator=gen, device=dev).to(torch.bfloat16) for _ in range(layers)]
+        return kp, vp
+
+    def oracle_seconds(fn, min_seconds=1.0):
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= min_seconds:
+                return el / runs
+
+    def append_leg(w, slots, kp, vp):
+        T = len(slots)
+        gen = torch.Generator(device=dev).manual_seed(w.seed + 100)
+        kn = torch.randn((T, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        vn = torch.randn((T, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(torch.bfloat16)
+        sd = torch.from_numpy(slots).to(dev)
+        us = replay_timed(lambda: [pa.prepare_cache_append(kn, vn, sd, kp[l], vp[l])
+                                   for l in range(layers)], args.kernel_reps) / layers
+        row = w.num_kv_heads * w.head_dim * 2
+        nbytes = 2 * 2 * T * row  # K and V rows: read from k, v and written to the pools
+        kc = np.zeros((w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim), np.uint16)
+        vc = np.zeros_like(kc)
+        kh = np.zeros((T, w.num_kv_heads, w.head_dim), np.uint16)
+        o_us = oracle_seconds(lambda: oc.cache_append(kc, vc, kh, kh, slots, w.block_size)) * 1e6
+        return {"tokens": T, "us_per_call": round(us, 3), "bytes": nbytes,
+                "GB/s": round(nbytes / us / 1e3, 1), "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                "oracle_us": round(o_us, 1)}
+
+    out = {}
+    # ---- the worked batch: one decode step
+    w = W.llama3_8b_decode(with_values=False)
+    w.script.append(("reserve", list(range(w.batch)), [1] * w.batch,
+                     np.arange(w.batch, dtype=np.int64)))
+    slots, pairs, med = host_reserve(w, 20)
+    kp, vp = device_pools(w)
+    out["llama3_8b_step"] = {"a1_reserve_host_us": {k: round(v, 1) for k, v in med.items()},
+                             "a3_append": append_leg(w, slots, kp, vp)}
+    del kp, vp
+    log(f"llama3_8b step: {out['llama3_8b_step']}")
+
+    # ---- prefix sharing: the first step after the forks (copy-on-write)
+    w = W.prefix_sharing(with_values=False)
+    slots, pairs, med = host_reserve(w, 5)
+    kp, vp = device_pools(w)
+    P = len(pairs)
+    pd = torch.from_numpy(np.ascontiguousarray(pairs)).to(dev)
+    us = replay_timed(lambda: [pa.prepare_copy_blocks(pd, P, kp[l], vp[l]) for l in range(layers)],
+                      args.kernel_reps) / layers
+    blk = w.num_kv_heads * w.block_size * w.head_dim * 2
+    cbytes = 2 * 2 * P * blk  # K and V blocks, each read once and written once
+    kc = np.zeros((w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim), np.uint16)
+    vc = np.zeros_like(kc)
+    o_us = oracle_seconds(lambda: oc.copy_blocks(kc, vc, pairs)) * 1e6
+    copy = {"pairs": P, "us_per_call": round(us, 3), "bytes": cbytes,
+            "GB/s": round(cbytes / us / 1e3, 1), "frac_of_hbm_peak": round(cbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+            "oracle_us": round(o_us, 1)}
+    out["prefix_sharing_p2056_first_step"] = {
+        "a1_reserve_host_us": {k: round(v, 1) for k, v in med.items()},
+        "a2_copy_blocks": copy, "a3_append": append_leg(w, slots, kp, vp)}
+    del kp, vp
+    log(f"prefix sharing: {out['prefix_sharing_p2056_first_step']}")
+
+    # ---- serving batch: one token for each of 256 sequences, and the upload
+    w = W.serving_batch(with_values=False)
+    slots, pairs, med = host_reserve(w, 5)
+    kp, vp = device_pools(w)
+    ent = {"a1_reserve_host_us": {k: round(v, 1) for k, v in med.items()},
+           "a3_append": append_leg(w, slots, kp, vp)}
+    del kp, vp
+    a = pa.Allocator(w.num_blocks, w.block_size, w.free_order)
+    replay(a, w.script, a.seq_fork, lambda s, n: a.seq_reserve(s, n, cow_cap=len(s)))
+    maxb = max(len(a.seq_block_table(s)) for s in w.seq_ids)
+    tab = torch.empty((w.batch, maxb), dtype=torch.int32, pin_memory=True)
+    lens = torch.empty(w.batch, dtype=torch.int32, pin_memory=True)
+    sl = torch.from_numpy(slots).pin_memory()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        a.build_block_tables(w.seq_ids, maxb, tables_out=tab.numpy(), lens_out=lens.numpy())
+    build_us = (time.perf_counter() - t0) / 20 * 1e6
+    o = oa.BlockAllocator(w.num_blocks, w.block_size, w.free_order)
+    replay(o, w.script, o.seq_fork, o.seq_reserve)
+    ob_us = oracle_seconds(lambda: o.block_tables(w.seq_ids, maxb)) * 1e6
+    td = torch.empty_like(tab, device=dev)
+    ld = torch.empty_like(lens, device=dev)
+    sd = torch.empty_like(sl, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        td.copy_(tab, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.kernel_reps):
+        td.copy_(tab, non_blocking=True)
+        ld.copy_(lens, non_blocking=True)
+        sd.copy_(sl, non_blocking=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    up_us = e0.elapsed_time(e1) * 1e3 / args.kernel_reps
+    ubytes = tab.numel() * 4 + lens.numel() * 4 + sl.numel() * 8
+    live = int(sum(len(a.seq_block_table(s)) for s in w.seq_ids)) * 4
+    a.close()
+    ent["a4_metadata"] = {"tables_shape": [w.batch, maxb], "build_tables_host_us": round(build_us, 1),
+                          "oracle_build_tables_us": round(ob_us, 1),
+                          "upload_us": round(up_us, 2), "upload_bytes": ubytes,
+                          "live_table_bytes": live,
+                          "upload_GB/s": round(ubytes / up_us / 1e3, 2)}
+    out["serving_batch_step"] = ent
+    log(f"serving batch: {ent}")
+
+    cp = out["prefix_sharing_p2056_first_step"]["a2_copy_blocks"]
+    print(json.dumps({
+        "metric": CACHE_OPS_METRIC, "value": cp["GB/s"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.kernel_reps * layers, "warmup": 1, "ms_per_step": round(cp["us_per_call"] / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"cache_ops: {layers} layer pools, graph replay; value = "
+                               "pa_copy_blocks of the prefix-sharing batch's 127 copy-on-write "
+                               "pairs (bytes read + written)", "rows": out},
+        "roofline": {"bound": "hbm", "achieved": cp["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": cp["frac_of_hbm_peak"], "traffic": None,
+                     "kernel": "pa_copy_blocks (copy_blocks_kernel), one layer"},
+        "cpu_baseline": {"value": round(cbytes / cp["oracle_us"] / 1e3, 4), "unit": "GB/s",
+                         "cores": 1, "kind": "oracle",
+                         "sample": "the oracle's copy_blocks of the same 127 pairs (NumPy, one "
+                                   "thread), repeated for about 1 s"}}), flush=True)
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -611,7 +817,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.workload != "llama3_8b_decode":  # kernel legs on other workloads
-        if args.layers == 32:
+        if args.layers == 32 and args.workload != "cache_ops":
             args.layers = 2  # each of these batches is larger than the last-level cache
         if "prefill" in args.workload:
             prefill_workload(args)
@@ -619,6 +825,8 @@ def main():
             swap_workload(args)
         elif args.workload == "prefix_cache_p2056":
             prefix_cache_workload(args)
+        elif args.workload == "cache_ops":
+            cache_ops_workload(args)
         else:
             other_workload(args)
         return
