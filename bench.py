@@ -584,8 +584,15 @@ def prefill_workload(args):
     td = torch.from_numpy(tables).to(dev)
     ld = torch.from_numpy(lens).to(dev)
     qsd = torch.from_numpy(qs).to(dev)
+    # pa_prefill_split: splits the key range of long query blocks when the
+    # call has too few query blocks to fill the GPU (the short chunks), and
+    # is pa_prefill otherwise (its workspace is then empty).
+    ws = pa.prefill_split_workspace(kp[0], w.batch, H_q, T, tables.shape[1])
+    ws_bytes = pa.pa_prefill_split_workspace_size(pa.cache_desc(kp[0]), w.batch, H_q, T,
+                                                  tables.shape[1])
     us = replay_timed(lambda: [pa.prepare_prefill(q, kp[l], vp[l], td, ld, qsd, w.block_size,
-                                                  w.scale, outs[l]) for l in range(args.layers)],
+                                                  w.scale, outs[l], workspace=ws)
+                               for l in range(args.layers)],
                       args.kernel_reps) / args.layers
     flops = prefill_flops(lens, nq, H_q, D)
     tfs = flops / (us * 1e-6) / 1e12
@@ -600,10 +607,13 @@ def prefill_workload(args):
                                "graph replay; "
                                "32 Q / 8 KV heads, head 128, bs 16, bf16",
                    "batch": w.batch, "query_tokens": T, "cache_tokens": int(lens.sum()),
-                   "query_tokens_per_seq": nq.tolist(), "us_per_call": round(us, 3)},
+                   "query_tokens_per_seq": nq.tolist(), "us_per_call": round(us, 3),
+                   "entry_point": "pa_prefill_split" + (" (key range split, workspace "
+                                                        f"{ws_bytes} B)" if ws_bytes else
+                                                        " (not split: runs as pa_prefill)")},
         "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "pa_prefill (one kernel), one layer",
+                     "traffic": None, "kernel": "pa_prefill_split (attention kernel, plus the merge kernel when split), one layer",
                      "us_per_launch": round(us, 3), "algorithmic_flops_per_call": flops},
     }
     if not args.no_cpu_baseline and not f16:

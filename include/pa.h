@@ -198,14 +198,49 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
  *               num_query_tokens (values are clamped into that range; n_b is
  *               clamped to [0, L]; L to max_blocks_per_seq * block_size).
  * block_tables, context_lens, block_size, desc: as for pa_decode.
- * num_seqs at most 8192.  No workspace: one wave computes each (sequence, KV
- * head, 16-query-row tile) over its whole causal key range.  n_b == 1 for
- * every sequence is decode.  num_query_tokens == 0 enqueues nothing. */
+ * num_seqs at most 8192.  No workspace: one workgroup computes each
+ * (sequence, KV head, query block of 16-32 tokens) over its whole causal key
+ * range, longest sequences first when num_seqs <= 256.  n_b == 1 for every
+ * sequence is decode.  num_query_tokens == 0 enqueues nothing. */
 pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
                      int32_t num_query_tokens, int32_t block_size, float scale, void* out,
                      int32_t num_q_heads, const pa_cache_desc* desc, void* stream);
+
+/* pa_prefill with long query blocks split along the keys (same arguments,
+ * same result up to fp32 summation order), for calls with few query tokens
+ * against long contexts (chunked prefill).  When the call has few query
+ * blocks (at most 640 (query block of 16 rows, KV head) items, bounded from
+ * num_query_tokens and num_seqs), the key range of each query block is cut
+ * into pieces of at least 48 key tiles of 32 keys; each piece is computed by
+ * its own workgroup into the workspace (per row: the softmax reference
+ * maximum, the sum and the unnormalised output), and a second kernel on the
+ * same stream merges the pieces (out = sum_i 2^(m_i - M) o_i /
+ * sum_i 2^(m_i - M) l_i, M = max_i m_i).  Otherwise it runs exactly as
+ * pa_prefill and leaves the workspace alone.
+ * workspace:    device scratch of at least pa_prefill_split_workspace_size()
+ *               bytes (0 when the shape is not split; then it may be NULL),
+ *               256-byte aligned, needing no initialisation; calls that
+ *               share it must be ordered on one stream.
+ * The number of pieces is bounded from host-known sizes only (num_seqs,
+ * num_query_tokens, max_blocks_per_seq), so the workspace size and the grid
+ * depend on them, not on the lengths' values.  query_start must be
+ * non-decreasing: with overlapping query ranges pieces past that bound are
+ * not computed and their rows are left unwritten (never out of bounds). */
+pa_status pa_prefill_split(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, const int32_t* query_start,
+                           int32_t num_seqs, int32_t num_query_tokens, int32_t block_size,
+                           float scale, void* out, int32_t num_q_heads,
+                           const pa_cache_desc* desc, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Bytes of workspace pa_prefill_split needs for this shape (0 when it would
+ * not split). */
+pa_status pa_prefill_split_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_query_tokens,
+                                          int32_t max_blocks_per_seq, size_t* bytes);
 
 /* Bytes of workspace pa_decode needs for this shape (independent of the
  * lengths' values). */

@@ -72,6 +72,10 @@ SIGNATURES = {
     "pa_decode_workspace_size": (_I32, [_PDESC, _I32, _I32, _I32, _c.POINTER(_c.c_size_t)]),
     "pa_prefill": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _c.c_float, _P, _I32,
                           _PDESC, _P]),
+    "pa_prefill_split": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _c.c_float, _P,
+                                _I32, _PDESC, _P, _c.c_size_t, _P]),
+    "pa_prefill_split_workspace_size": (_I32, [_PDESC, _I32, _I32, _I32, _I32,
+                                               _c.POINTER(_c.c_size_t)]),
     "pa_allocator_create": (_I32, [_I32, _I32, _PI32, _c.POINTER(_P)]),
     "pa_allocator_destroy": (None, [_P]),
     "pa_seq_create": (_I32, [_P, _I64]),
@@ -299,9 +303,42 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, blo
     return out
 
 
+def pa_prefill_split_workspace_size(desc, num_seqs, num_q_heads, num_query_tokens,
+                                    max_blocks_per_seq):
+    n = ctypes.c_size_t(0)
+    _check(load_library().pa_prefill_split_workspace_size(
+        ctypes.byref(desc), num_seqs, num_q_heads, num_query_tokens, max_blocks_per_seq,
+        ctypes.byref(n)))
+    return n.value
+
+
+def prefill_split_workspace(k_cache, num_seqs, num_q_heads, num_query_tokens,
+                            max_blocks_per_seq):
+    """Allocates (with torch) a workspace sized for pa_prefill_split on this
+    shape (at least 256 bytes; it needs no initialisation)."""
+    torch = _torch()
+    n = pa_prefill_split_workspace_size(cache_desc(k_cache), num_seqs, num_q_heads,
+                                        num_query_tokens, max_blocks_per_seq)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=k_cache.device)
+
+
+def pa_prefill_split(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size,
+                     scale, out, workspace=None, stream=None):
+    """pa_prefill with the key range of long query blocks split over several
+    workgroups and merged (for few query tokens against long contexts);
+    allocates the workspace with torch when none is given."""
+    if workspace is None:
+        workspace = prefill_split_workspace(k_cache, context_lens.numel(), q.shape[1], q.shape[0],
+                                            block_tables.shape[1])
+    prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size,
+                    scale, out, stream, workspace=workspace)()
+    return out
+
+
 def prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size,
-                    scale, out, stream=None):
-    """pa_prefill with its arguments checked and fixed (see pa_prefill)."""
+                    scale, out, stream=None, workspace=None):
+    """pa_prefill (or pa_prefill_split, when a workspace tensor is given) with
+    its arguments checked and fixed (see pa_prefill)."""
     torch = _torch()
     _same_pool(k_cache, v_cache)
     desc = cache_desc(k_cache)
@@ -320,10 +357,13 @@ def prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start
     args = (_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables"), block_tables.shape[1],
             _dev(context_lens, "context_lens"), _dev(query_start, "query_start"), B, T,
-            int(block_size), ctypes.c_float(scale), _dev(out, "out"), H_q, ctypes.byref(desc),
-            _stream(stream))
-    return PreparedCall(lib.pa_prefill, args, (q, k_cache, v_cache, block_tables, context_lens,
-                                               query_start, out, desc))
+            int(block_size), ctypes.c_float(scale), _dev(out, "out"), H_q, ctypes.byref(desc))
+    keep = (q, k_cache, v_cache, block_tables, context_lens, query_start, out, desc)
+    if workspace is None:
+        return PreparedCall(lib.pa_prefill, args + (_stream(stream),), keep)
+    args += (_dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+             _stream(stream))
+    return PreparedCall(lib.pa_prefill_split, args, keep + (workspace,))
 
 
 # --------------------------------------------------------------- allocator

@@ -32,6 +32,7 @@
 // takes bf16 or fp16 pools.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -69,10 +70,17 @@ constexpr int64_t kMinItemsR2 = 512;
 constexpr int kSortMax = 256;
 static_assert(kSortMax <= kNW * kWave, "one sequence per thread while ranking");
 
-// Bytes of the LDS header (per-sequence snapshot) in front of the K/V tiles.
-__host__ __device__ constexpr int32_t header_bytes(int32_t B) {
-  return ((3 * B + 1 + kNW + (B <= kSortMax ? B : 0)) * 4 + 15) & ~15;
+// Bytes of the LDS header (per-sequence snapshot) in front of the K/V tiles:
+// query starts, query counts, prefix sums, wave totals, the processing
+// order (up to kSortMax sequences) and, when long items are split along the
+// keys, each sequence's number of pieces.
+__host__ __device__ constexpr int32_t header_bytes(int32_t B, bool split) {
+  return ((3 * B + 1 + kNW + (B <= kSortMax ? B : 0) + (split ? B : 0)) * 4 + 15) & ~15;
 }
+
+// Rows of one workgroup's partial state when items are split (one 16-row
+// block per wave).
+constexpr int kPieceRows = kNW * 16;
 
 struct PrefillArgs {
   const void* q;            // [T][H_q][D]
@@ -86,6 +94,12 @@ struct PrefillArgs {
   int32_t max_blocks;
   int32_t G;
   float scale_log2;         // scale * log2(e)
+  // Split items only: key tiles per piece, and per workgroup (piece) and
+  // row its unnormalised output [grid][kPieceRows][D] and its reference
+  // maximum (log2 units) and sum [grid][kPieceRows][2].
+  int32_t key_tiles;
+  float* ws_o;
+  float* ws_ml;
 };
 
 template <int D>
@@ -116,34 +130,43 @@ __device__ __forceinline__ int32_t find_item_seq(const int32_t* P, int32_t B, in
   return lo;
 }
 
-template <int E, int D, int GP, int R>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kOcc, kOcc)))
-prefill_kernel(PrefillArgs a) {
-  using Geo = TileGeo<D>;
-  constexpr int kBlk = Geo::kBlk, kDS = Geo::kDS, kLoads = Geo::kLoads;
-  constexpr int TP = 16 / GP;          // query tokens per 16-row block
-  constexpr int QW = R * TP;           // query tokens per wave
-  constexpr int QT = kNW * QW;         // query tokens per workgroup
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), v = tid >> 6;
-  const int jr = lane >> 4, c16 = lane & 15;
-  const int32_t B = a.B, H_kv = a.pool.H_kv, G = a.G, H_q = H_kv * G;
-  const int log2_bs = a.pool.log2_bs;
-  const int32_t len_cap = a.max_blocks << log2_bs;
+// One work item: key tiles [t_lo, t_hi) for the query tokens [i0, i1) of
+// sequence b (query rows from qs on, nq query tokens, L cache tokens)
+// against KV head kvh; piece s of the S pieces of its query block (S = 1
+// when items are not split).
+struct Item {
+  int32_t b, kvh, qs, nq, L, i0, i1, t_lo, t_hi, s, S;
+};
 
+// Key tiles a query block sees: keys 0 .. the position of its last token.
+__device__ __forceinline__ int32_t block_tiles(int32_t L, int32_t nq, int32_t qb, int32_t QT) {
+  return (L - nq + min((qb + 1) * QT, nq) - 1) / kKT + 1;
+}
+
+// The workgroup prologue of the attention and merge kernels: the
+// per-sequence snapshot in the LDS header, the processing order, and the
+// item of workgroup blockIdx.x.  Returns false (for the whole workgroup)
+// when blockIdx.x is past the last item.  QT: query tokens per query
+// block; kSplit: query blocks are cut into pieces of a.key_tiles key tiles.
+template <int QT, bool kSplit>
+__device__ bool locate_item(const PrefillArgs& a, char* smem, Item& it) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), v = tid >> 6;
+  const int32_t B = a.B, H_kv = a.pool.H_kv;
+  const int32_t len_cap = a.max_blocks << a.pool.log2_bs;
+  const int32_t kt_per = kSplit ? a.key_tiles : 1;
   // LDS: per sequence the query start and the number of query tokens n_b
-  // (clamped to [0, L_b]); the exclusive prefix sums of query blocks in
+  // (clamped to [0, L_b]); the exclusive prefix sums of its items in
   // processing order; for short batches the processing order itself (ORD:
   // rank -> sequence, longest sequence first, so that the items that walk
-  // the most key tiles start first and the grid ends on short ones); then
-  // the two K/V tile stages.
+  // the most key tiles start first and the grid ends on short ones); for
+  // split items each sequence's number of pieces.
   const bool sorted = B <= kSortMax;
   int32_t* QS = reinterpret_cast<int32_t*>(smem);  // [B]
   int32_t* NQ = QS + B;                            // [B]
   int32_t* PQ = NQ + B;                            // [B + 1]
   int32_t* misc = PQ + B + 1;                      // [kNW]
   int32_t* ORD = misc + kNW;                       // [B] when sorted
-  char* tiles = smem + header_bytes(B);
+  int32_t* NP = ORD + (sorted ? B : 0);            // [B] when split
   for (int32_t b = tid; b < B; b += kThreads) {
     const int32_t q0 = min(max(a.qstart[b], 0), a.T);
     const int32_t q1 = min(max(a.qstart[b + 1], q0), a.T);
@@ -152,6 +175,11 @@ prefill_kernel(PrefillArgs a) {
     QS[b] = q0;
     NQ[b] = n;
     PQ[b] = n > 0 ? L : -1;  // ranking key, replaced by the prefix sums below
+    if constexpr (kSplit) {
+      int32_t np = 0;
+      for (int32_t qb = 0; qb * QT < n; ++qb) np += (block_tiles(L, n, qb, QT) + kt_per - 1) / kt_per;
+      NP[b] = np;
+    }
   }
   __syncthreads();
   if (sorted) {
@@ -173,7 +201,10 @@ prefill_kernel(PrefillArgs a) {
   for (int32_t c = 0; c < B; c += kThreads) {
     const int32_t r = c + tid;
     int32_t nt = 0;
-    if (r < B) nt = (NQ[sorted ? ORD[r] : r] + QT - 1) / QT;
+    if (r < B) {
+      const int32_t b = sorted ? ORD[r] : r;
+      nt = kSplit ? NP[b] : (NQ[b] + QT - 1) / QT;
+    }
     const int32_t incl = pa::wave_incl_scan(nt);
     if (lane == kWave - 1) misc[v] = incl;
     __syncthreads();
@@ -191,21 +222,66 @@ prefill_kernel(PrefillArgs a) {
   if (tid == 0) PQ[B] = carry;
   __syncthreads();
 
-  // ---- this workgroup's item: (b, kvh, query block qb); sequences in
-  // processing order, each one's query blocks longest first
+  // ---- this workgroup's item: sequences in processing order, each one's
+  // query blocks longest first; a query block's items are its pieces (in
+  // key order) times the KV heads.
   const int32_t items = uni(PQ[B]) * H_kv;
   const int32_t f = blockIdx.x;
-  if (f >= items) return;  // the whole workgroup
+  if (f >= items) return false;
   const int32_t rk = uni(find_item_seq(PQ, B, H_kv, f));
-  const int32_t b = sorted ? uni(ORD[rk]) : rk;
-  const int32_t local = f - uni(PQ[rk]) * H_kv;
-  const int32_t kvh = local % H_kv;
-  const int32_t nq = uni(NQ[b]);
-  const int32_t qb = (nq + QT - 1) / QT - 1 - local / H_kv;
-  const int32_t L = min(max(a.lens[b], 0), len_cap);  // uniform (scalar load)
-  const int32_t pbase = L - nq;                        // position of query token 0
-  const int32_t i0 = qb * QT, i1 = min(i0 + QT, nq);   // the workgroup's tokens
-  const int32_t ntiles = (pbase + i1 - 1) / kKT + 1;   // keys 0 .. its last position
+  it.b = sorted ? uni(ORD[rk]) : rk;
+  int32_t local = f - uni(PQ[rk]) * H_kv;
+  it.nq = uni(NQ[it.b]);
+  it.qs = uni(QS[it.b]);
+  it.L = min(max(a.lens[it.b], 0), len_cap);  // uniform (scalar load)
+  int32_t qb = (it.nq + QT - 1) / QT - 1;
+  if constexpr (kSplit) {
+    int32_t np = (block_tiles(it.L, it.nq, qb, QT) + kt_per - 1) / kt_per;
+    while (qb > 0 && local >= np * H_kv) {
+      local -= np * H_kv;
+      --qb;
+      np = (block_tiles(it.L, it.nq, qb, QT) + kt_per - 1) / kt_per;
+    }
+    it.S = np;
+    it.s = local / H_kv;
+    it.kvh = local - it.s * H_kv;
+    if (it.s >= it.S) return false;  // only if the snapshot disagreed with itself
+  } else {
+    it.kvh = local % H_kv;
+    qb -= local / H_kv;
+    it.s = 0;
+    it.S = 1;
+  }
+  it.i0 = qb * QT;
+  it.i1 = min(it.i0 + QT, it.nq);
+  const int32_t ntiles = block_tiles(it.L, it.nq, qb, QT);
+  it.t_lo = kSplit ? it.s * kt_per : 0;
+  it.t_hi = kSplit ? min(it.t_lo + kt_per, ntiles) : ntiles;
+  return true;
+}
+
+template <int E, int D, int GP, int R, bool kSplit>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kOcc, kOcc)))
+prefill_kernel(PrefillArgs a) {
+  static_assert(!kSplit || R == 1, "split items take one row block per wave");
+  using Geo = TileGeo<D>;
+  constexpr int kBlk = Geo::kBlk, kDS = Geo::kDS, kLoads = Geo::kLoads;
+  constexpr int TP = 16 / GP;          // query tokens per 16-row block
+  constexpr int QW = R * TP;           // query tokens per wave
+  constexpr int QT = kNW * QW;         // query tokens per workgroup
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), v = tid >> 6;
+  const int jr = lane >> 4, c16 = lane & 15;
+  const int32_t H_kv = a.pool.H_kv, G = a.G, H_q = H_kv * G;
+  const int log2_bs = a.pool.log2_bs;
+
+  Item it;
+  if (!locate_item<QT, kSplit>(a, smem, it)) return;
+  char* tiles = smem + header_bytes(a.B, kSplit);
+  const int32_t b = it.b, kvh = it.kvh, nq = it.nq, L = it.L;
+  const int32_t pbase = L - nq;                       // position of query token 0
+  const int32_t i0 = it.i0, i1 = it.i1;               // the workgroup's tokens
+  const int32_t tlo = it.t_lo, nloc = it.t_hi - it.t_lo;  // its key tiles
   // This wave's tokens [w0, w1) and positions.
   const int32_t w0 = i0 + v * QW, w1 = min(w0 + QW, i1);
   const bool wave_live = w0 < w1;
@@ -222,7 +298,7 @@ prefill_kernel(PrefillArgs a) {
   u32x4_t qf[R][kDS];
   int32_t lim[R];
   {
-    const int32_t qs_b = uni(QS[b]);
+    const int32_t qs_b = it.qs;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int32_t ti = w0 + r * TP + c16 / GP, g = c16 % GP;
@@ -251,15 +327,16 @@ prefill_kernel(PrefillArgs a) {
   const char* kbase = reinterpret_cast<const char*>(a.pool.k_cache) + col0 * 16;
   const char* vbase = reinterpret_cast<const char*>(a.pool.v_cache) + col0 * 16;
   const int32_t nb1 = a.pool.num_blocks - 1;
+  // Tile indices kt below count from the item's first key tile, tlo.
   auto table_entry = [&](int32_t kt) __attribute__((always_inline)) -> int32_t {
-    const int32_t key = min(kt * kKT + my_row, L - 1);
+    const int32_t key = min((tlo + kt) * kKT + my_row, L - 1);
     return trow[min(key >> log2_bs, a.max_blocks - 1)];
   };
   // Every lane loads (the row is clamped into the cache), so the number of
   // loads in flight is the same on every path; stash zeroes rows past it.
   auto gather = [&](int32_t kt, int32_t tb, u32x4_t (&kr)[kLoads],
                     u32x4_t (&vr)[kLoads]) __attribute__((always_inline)) {
-    const int32_t key = min(kt * kKT + my_row, L - 1);
+    const int32_t key = min((tlo + kt) * kKT + my_row, L - 1);
     const uint32_t row = (uint32_t)(min(max(tb, 0), nb1) * rows_per_block + kv_row) +
                          (uint32_t)(key & bs_mask);
     const uint64_t off = (uint64_t)row * Geo::kRowBytes;
@@ -273,8 +350,8 @@ prefill_kernel(PrefillArgs a) {
   auto stash = [&](int32_t kt, int stage, const u32x4_t (&kr)[kLoads],
                    const u32x4_t (&vr)[kLoads]) __attribute__((always_inline)) {
     char* kl = tiles + stage * Geo::kStage + lds_off;
-    if (kt * kKT + kKT > L) {  // uniform: the tile reaches past the cache
-      const bool in = kt * kKT + my_row < L;
+    if ((tlo + kt) * kKT + kKT > L) {  // uniform: the tile reaches past the cache
+      const bool in = (tlo + kt) * kKT + my_row < L;
 #pragma unroll
       for (int h = 0; h < kLoads; ++h) {
         *reinterpret_cast<u32x4_t*>(kl + h * kPieceStep) = in ? kr[h] : u32x4_t{0, 0, 0, 0};
@@ -456,8 +533,10 @@ prefill_kernel(PrefillArgs a) {
     tb[1 - p] = table_entry(kt + N + 1);
     gather(kt + N, tb[p], kr[x], vr[x]);
     pa::lds_barrier();
-    const int32_t t0 = kt * kKT;
-    if (wave_live && t0 <= wp_max) {
+    const int32_t t0 = (tlo + kt) * kKT;
+    // Spare tiles past the item's last (kt >= nloc) compute nothing: for a
+    // piece of a split query block they are the next piece's keys.
+    if (wave_live && kt < nloc && t0 <= wp_max) {
       if (front(p, t0, t0 + kKT - 1 > wp_min)) return true;
       back();
     }
@@ -475,7 +554,7 @@ prefill_kernel(PrefillArgs a) {
   // their registers across iterations; the count is rounded up to a
   // multiple of N (spare last tiles compute nothing), and every wave passes
   // exactly one barrier per tile on every path.
-  const int32_t ntot = (ntiles + N - 1) / N * N;
+  const int32_t ntot = (nloc + N - 1) / N * N;
   int32_t kt = 0;
   while (true) {
     bool brk = false;
@@ -509,6 +588,30 @@ prefill_kernel(PrefillArgs a) {
   // ---- finish: row block r, lane 16j + c, register q holds row 4j + q at
   // columns kBlk * c .. kBlk * c + kBlk - 1; its normaliser is l[r][q].
   if (!wave_live) return;
+  if constexpr (kSplit) {
+    if (it.S > 1) {
+      // A piece of a split query block: per row its reference maximum (the
+      // base of the exponentials in acc and l), l and the unnormalised
+      // output, for the merge kernel.
+      const int64_t base = (int64_t)blockIdx.x * kPieceRows + v * 16;
+      pa::static_for<0, 4>([&](auto Q) {
+        constexpr int q = decltype(Q)::value;
+        const int row = 4 * jr + q;
+        const float refq = pa::pick_row_quad<q>(ref[0], jr);  // row 4j + q
+        const int32_t ti = w0 + row / GP, g = row % GP;
+        if (ti < w1 && g < G) {
+          floatx4_t* o = reinterpret_cast<floatx4_t*>(a.ws_o + (base + row) * D + kBlk * c16);
+#pragma unroll
+          for (int k = 0; k < kBlk / 4; ++k)
+            o[k] = floatx4_t{acc[0][4 * k][q], acc[0][4 * k + 1][q], acc[0][4 * k + 2][q],
+                             acc[0][4 * k + 3][q]};
+          if (c16 == 0)
+            *reinterpret_cast<f32x2_t*>(a.ws_ml + (base + row) * 2) = f32x2_t{refq, l[0][q]};
+        }
+      });
+      return;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     pa::static_for<0, 4>([&](auto Q) {
@@ -523,7 +626,7 @@ prefill_kernel(PrefillArgs a) {
           pk[k] = pa::pack2<E>(acc[r][2 * k][q] * inv, acc[r][2 * k + 1][q] * inv);
         }
         char* dst = reinterpret_cast<char*>(a.out) +
-                    (((int64_t)(uni(QS[b]) + ti) * H_q + kvh * G + g) * D + kBlk * c16) * 2;
+                    (((int64_t)(it.qs + ti) * H_q + kvh * G + g) * D + kBlk * c16) * 2;
         if constexpr (kBlk == 8) *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
         else *reinterpret_cast<uint2*>(dst) = uint2{pk[0], pk[1]};
       }
@@ -531,10 +634,62 @@ prefill_kernel(PrefillArgs a) {
   }
 }
 
-template <int E, int D, int GP, int R>
+// Combines the pieces of a split query block: workgroup f runs only if it
+// holds piece 0 of a query block cut into S > 1 pieces, whose pieces are
+// the workgroups f, f + H_kv, ..., f + (S - 1) H_kv of the attention grid.
+// Thread t merges row t / 4 of the workgroup's rows, columns
+// (t % 4) * D/4 .. + D/4:  M = max_s m_s,  out = sum_s 2^(m_s - M) o_s /
+// sum_s 2^(m_s - M) l_s, rounded once to the output format.
+template <int E, int D, int GP>
+__global__ void __launch_bounds__(kThreads) prefill_merge_kernel(PrefillArgs a) {
+  constexpr int TP = 16 / GP, QT = kNW * TP;
+  constexpr int C = D / 4, NC = C / 4;  // columns per thread, as float4 chunks
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  Item it;
+  if (!locate_item<QT, true>(a, smem, it)) return;
+  if (it.S <= 1 || it.s != 0) return;
+  const int32_t H_kv = a.pool.H_kv;
+  if ((int64_t)blockIdx.x + (int64_t)(it.S - 1) * H_kv >= gridDim.x) return;  // malformed snapshot
+  const int row = threadIdx.x >> 2, part = threadIdx.x & 3;
+  const int rr = row & 15;
+  const int32_t ti = it.i0 + (row >> 4) * TP + rr / GP, g = rr % GP;
+  if (ti >= it.i1 || g >= a.G) return;
+  float M = -3.0e38f;
+  for (int32_t s = 0; s < it.S; ++s) {
+    const int64_t slot = ((int64_t)blockIdx.x + (int64_t)s * H_kv) * kPieceRows + row;
+    M = fmaxf(M, a.ws_ml[slot * 2]);
+  }
+  floatx4_t o[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) o[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int32_t s = 0; s < it.S; ++s) {
+    const int64_t slot = ((int64_t)blockIdx.x + (int64_t)s * H_kv) * kPieceRows + row;
+    const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(a.ws_ml + slot * 2);
+    const float w = __builtin_amdgcn_exp2f(ml[0] - M);  // 0 for a piece with no keys here
+    l = fmaf(w, ml[1], l);
+    const floatx4_t* src = reinterpret_cast<const floatx4_t*>(a.ws_o + slot * D + part * C);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) o[c] += w * src[c];
+  }
+  const float inv = 1.f / l;
+  const int32_t H_q = H_kv * a.G;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(
+      reinterpret_cast<char*>(a.out) +
+      (((int64_t)(it.qs + ti) * H_q + it.kvh * a.G + g) * D + part * C) * 2);
+#pragma unroll
+  for (int c = 0; c < NC; c += 2) {
+    const floatx4_t x = o[c] * inv, y = o[c + 1] * inv;
+    *reinterpret_cast<u32x4_t*>(dst + 2 * c) =
+        u32x4_t{pa::pack2<E>(x[0], x[1]), pa::pack2<E>(x[2], x[3]), pa::pack2<E>(y[0], y[1]),
+                pa::pack2<E>(y[2], y[3])};
+  }
+}
+
+template <int E, int D, int GP, int R, bool kSplit = false>
 pa_status launch_r(const PrefillArgs& a, int64_t items, hipStream_t s) {
-  auto kern = prefill_kernel<E, D, GP, R>;
-  const size_t lds = (size_t)header_bytes(a.B) + 2 * TileGeo<D>::kStage;
+  auto kern = prefill_kernel<E, D, GP, R, kSplit>;
+  const size_t lds = (size_t)header_bytes(a.B, kSplit) + 2 * TileGeo<D>::kStage;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -542,6 +697,9 @@ pa_status launch_r(const PrefillArgs& a, int64_t items, hipStream_t s) {
       return pa::fail(PA_ERR_DEVICE, "pa_prefill: LDS attribute: %s", hipGetErrorString(e));
   }
   hipLaunchKernelGGL(kern, dim3((uint32_t)items), dim3(kThreads), lds, s, a);
+  if constexpr (kSplit)
+    hipLaunchKernelGGL((prefill_merge_kernel<E, D, GP>), dim3((uint32_t)items), dim3(kThreads),
+                       (size_t)header_bytes(a.B, true), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_DEVICE, "pa_prefill: %s", hipGetErrorString(e));
   return PA_OK;
@@ -549,38 +707,91 @@ pa_status launch_r(const PrefillArgs& a, int64_t items, hipStream_t s) {
 
 // Work items for R row blocks per wave: at most ceil(T / QT) + B query
 // blocks per KV head (QT = 4 waves x R x 16 / GP tokens).
-inline int64_t prefill_items(const PrefillArgs& a, int GP, int R) {
+inline int64_t prefill_items(int32_t T, int32_t B, int32_t H_kv, int GP, int R) {
   const int64_t QT = (int64_t)kNW * R * (16 / GP);
-  return (((int64_t)a.T + QT - 1) / QT + a.B) * a.pool.H_kv;
+  return (((int64_t)T + QT - 1) / QT + B) * H_kv;
+}
+
+inline int group_pad(int32_t G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 8 ? 8 : 16; }
+
+inline size_t align_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+// How pa_prefill_split runs a call of this shape, from host-known sizes
+// only.  With at most kSplitMaxItems items of the one-row-block kernel (too
+// few to keep every CU busy through the longest query blocks), query
+// blocks are cut along the keys into pieces of key_tiles tiles: at least
+// kMinKeyTiles, and enough that the grid stays near kSplitGrid workgroups.
+// The grid bounds the pieces from above: every query block of the item
+// bound taken as seeing all ceil(max_blocks * block_size / 32) key tiles.
+// Each piece pays a fixed start (snapshot, query rows, the first tiles'
+// loads), and so does each workgroup past the real pieces, so pieces stay
+// long.  Measured on the worked batch (last N tokens of each sequence): N =
+// 64 took 51 us split against 91 us whole, N = 128 68 against 94 (pieces of
+// 48 tiles; 4-16 tile pieces were up to 4x slower), while N = 256 (928
+// items) took 100 us whole and 109-115 us split.  Tuning override (read on
+// every call): PA_PREFILL_KEY_TILES.
+struct SplitPlan {
+  bool split;
+  int32_t key_tiles;
+  int64_t grid;
+  size_t o_bytes, ws_bytes;
+};
+constexpr int64_t kSplitMaxItems = 640;
+constexpr int64_t kMinKeyTiles = 48;
+constexpr int64_t kSplitGrid = 1536;
+
+SplitPlan split_plan(const pa_cache_desc* d, int32_t B, int32_t H_q, int32_t T, int32_t maxb) {
+  SplitPlan p{false, 0, 0, 0, 0};
+  if (B <= 0 || T <= 0 || maxb < 1) return p;
+  const int32_t H_kv = d->num_kv_heads;
+  const int GP = group_pad(H_q / H_kv);
+  const int64_t items1 = prefill_items(T, B, H_kv, GP, 1);
+  if (items1 > kSplitMaxItems || prefill_items(T, B, H_kv, GP, 2) >= kMinItemsR2) return p;
+  const int64_t maxtiles = ((int64_t)maxb * d->block_size + kKT - 1) / kKT;
+  int64_t kt = std::max<int64_t>(kMinKeyTiles, (maxtiles * items1 + kSplitGrid - 1) / kSplitGrid);
+  if (const char* e = std::getenv("PA_PREFILL_KEY_TILES")) {
+    const int x = std::atoi(e);
+    if (x >= 1) kt = x;
+  }
+  const int64_t S = (maxtiles + kt - 1) / kt;
+  if (S <= 1 || items1 * S >= (1ll << 31)) return p;
+  p.split = true;
+  p.key_tiles = (int32_t)kt;
+  p.grid = items1 * S;
+  p.o_bytes = align_up((size_t)p.grid * kPieceRows * d->head_dim * sizeof(float), 256);
+  p.ws_bytes = p.o_bytes + align_up((size_t)p.grid * kPieceRows * 2 * sizeof(float), 256);
+  return p;
 }
 
 template <int E, int D, int GP>
-pa_status launch(const PrefillArgs& a, hipStream_t s) {
-  const int64_t items1 = prefill_items(a, GP, 1), items2 = prefill_items(a, GP, 2);
+pa_status launch(const PrefillArgs& a, const SplitPlan& plan, hipStream_t s) {
+  const int64_t items1 = prefill_items(a.T, a.B, a.pool.H_kv, GP, 1);
+  const int64_t items2 = prefill_items(a.T, a.B, a.pool.H_kv, GP, 2);
   if (items1 >= (1ll << 31))  // the kernel numbers items in int32
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: too many query blocks");
+  if (plan.split) return launch_r<E, D, GP, 1, true>(a, plan.grid, s);
   if (items2 >= kMinItemsR2) return launch_r<E, D, GP, 2>(a, items2, s);
   return launch_r<E, D, GP, 1>(a, items1, s);
 }
 
 template <int E, int D>
-pa_status dispatch_g(const PrefillArgs& a, hipStream_t s) {
-  if (a.G <= 1) return launch<E, D, 1>(a, s);
-  if (a.G <= 2) return launch<E, D, 2>(a, s);
-  if (a.G <= 4) return launch<E, D, 4>(a, s);
-  if (a.G <= 8) return launch<E, D, 8>(a, s);
-  return launch<E, D, 16>(a, s);
+pa_status dispatch_g(const PrefillArgs& a, const SplitPlan& plan, hipStream_t s) {
+  if (a.G <= 1) return launch<E, D, 1>(a, plan, s);
+  if (a.G <= 2) return launch<E, D, 2>(a, plan, s);
+  if (a.G <= 4) return launch<E, D, 4>(a, plan, s);
+  if (a.G <= 8) return launch<E, D, 8>(a, plan, s);
+  return launch<E, D, 16>(a, plan, s);
 }
 
-}  // namespace
-
-extern "C" {
-
-pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
-                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                     const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
-                     int32_t num_query_tokens, int32_t block_size, float scale, void* out,
-                     int32_t num_q_heads, const pa_cache_desc* desc, void* stream) {
+// Checks the arguments shared by pa_prefill and pa_prefill_split and fills
+// the kernel arguments; *nothing is set when the call has no work.
+pa_status prefill_args(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+                       int32_t num_query_tokens, int32_t block_size, float scale, void* out,
+                       int32_t num_q_heads, const pa_cache_desc* desc, PrefillArgs& a,
+                       bool* nothing) {
+  *nothing = false;
   pa_status st = pa_supported(desc, num_q_heads);
   if (st != PA_OK) return st;
   if (desc->dtype != PA_BF16 && desc->dtype != PA_F16)
@@ -598,14 +809,16 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
   if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
   if ((int64_t)desc->num_blocks * desc->num_kv_heads * block_size > INT32_MAX)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: pool of more than 2^31 rows per pool");
-  if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
+  if (num_seqs == 0 || num_query_tokens == 0) {
+    *nothing = true;
+    return PA_OK;
+  }
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");
   if (!pa::aligned(q, 16) || !pa::aligned(k_cache, 16) || !pa::aligned(v_cache, 16) ||
       !pa::aligned(out, 16) || !pa::aligned(block_tables, 4) || !pa::aligned(context_lens, 4) ||
       !pa::aligned(query_start, 4))
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "misaligned pointer");
-  PrefillArgs a;
   a.q = q;
   a.tables = block_tables;
   a.lens = context_lens;
@@ -618,10 +831,79 @@ pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
   a.max_blocks = max_blocks_per_seq;
   a.G = num_q_heads / desc->num_kv_heads;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.key_tiles = 0;
+  a.ws_o = nullptr;
+  a.ws_ml = nullptr;
+  return PA_OK;
+}
+
+pa_status run(const PrefillArgs& a, const SplitPlan& plan, const pa_cache_desc* desc,
+              void* stream) {
   hipStream_t s = (hipStream_t)stream;
   const bool d128 = desc->head_dim == 128;
-  if (desc->dtype == PA_F16) return d128 ? dispatch_g<2, 128>(a, s) : dispatch_g<2, 64>(a, s);
-  return d128 ? dispatch_g<1, 128>(a, s) : dispatch_g<1, 64>(a, s);
+  if (desc->dtype == PA_F16)
+    return d128 ? dispatch_g<2, 128>(a, plan, s) : dispatch_g<2, 64>(a, plan, s);
+  return d128 ? dispatch_g<1, 128>(a, plan, s) : dispatch_g<1, 64>(a, plan, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_prefill(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs,
+                     int32_t num_query_tokens, int32_t block_size, float scale, void* out,
+                     int32_t num_q_heads, const pa_cache_desc* desc, void* stream) {
+  PrefillArgs a;
+  bool nothing;
+  pa_status st = prefill_args(q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                              context_lens, query_start, num_seqs, num_query_tokens, block_size,
+                              scale, out, num_q_heads, desc, a, &nothing);
+  if (st != PA_OK || nothing) return st;
+  return run(a, SplitPlan{false, 0, 0, 0, 0}, desc, stream);
+}
+
+pa_status pa_prefill_split_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
+                                          int32_t num_q_heads, int32_t num_query_tokens,
+                                          int32_t max_blocks_per_seq, size_t* bytes) {
+  pa_status st = pa_supported(desc, num_q_heads);
+  if (st != PA_OK) return st;
+  if (!bytes) return pa::fail(PA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (num_seqs < 0 || num_query_tokens < 0 || max_blocks_per_seq < 1)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_seqs %d / num_query_tokens %d / "
+                    "max_blocks_per_seq %d", num_seqs, num_query_tokens, max_blocks_per_seq);
+  *bytes = split_plan(desc, num_seqs, num_q_heads, num_query_tokens, max_blocks_per_seq).ws_bytes;
+  return PA_OK;
+}
+
+pa_status pa_prefill_split(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, const int32_t* query_start,
+                           int32_t num_seqs, int32_t num_query_tokens, int32_t block_size,
+                           float scale, void* out, int32_t num_q_heads,
+                           const pa_cache_desc* desc, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  PrefillArgs a;
+  bool nothing;
+  pa_status st = prefill_args(q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                              context_lens, query_start, num_seqs, num_query_tokens, block_size,
+                              scale, out, num_q_heads, desc, a, &nothing);
+  if (st != PA_OK || nothing) return st;
+  const SplitPlan plan =
+      split_plan(desc, num_seqs, num_q_heads, num_query_tokens, max_blocks_per_seq);
+  if (plan.split) {
+    if (!workspace) return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL workspace");
+    if (!pa::aligned(workspace, 256))
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    if (workspace_bytes < plan.ws_bytes)
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace %zu bytes < %zu needed",
+                      workspace_bytes, plan.ws_bytes);
+    a.key_tiles = plan.key_tiles;
+    a.ws_o = reinterpret_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.o_bytes);
+  }
+  return run(a, plan, desc, stream);
 }
 
 }  // extern "C"

@@ -115,6 +115,53 @@ def test_prefill_validates_on_the_host():
     assert st_ == pa.PA_ERR_UNSUPPORTED and b"too many" in lib.pa_last_error()
 
 
+def test_prefill_split_plan_on_the_host():
+    """Workspace of pa_prefill_split: zero when the call has enough query
+    blocks or too few key tiles to split, else one piece per (query block
+    bound x ceil(key tiles / key_tiles)) with 64 rows of D + 2 floats; the
+    arguments are checked as for pa_prefill, plus the workspace."""
+    lib = pa.load_library()
+    d = pa.CacheDesc(4096, 16, 8, 128, pa.PA_BF16)
+
+    def size(B, Hq, T, maxb, desc=d):
+        n = ctypes.c_size_t(12345)
+        st_ = lib.pa_prefill_split_workspace_size(ctypes.byref(desc), B, Hq, T, maxb,
+                                                  ctypes.byref(n))
+        return st_, n.value
+
+    # The worked batch, last 64 tokens of each sequence: 498 query tokens, 16
+    # per query block -> (32 + 8) x 8 = 320 items; 257 blocks of 16 -> 129 key
+    # tiles -> pieces of max(48, ceil(129 x 320 / 1536) = 27) = 48 tiles -> 3
+    # per item: 960 pieces.  The 128-token chunk: 946 query tokens -> (60 + 8)
+    # x 8 = 544 items -> max(48, 46) = 48 tiles -> 1,632 pieces.
+    def ws(pieces):
+        return (-(-pieces * 64 * 128 * 4 // 256) * 256) + (-(-pieces * 64 * 2 * 4 // 256) * 256)
+
+    st_, n = size(8, 32, 498, 257)
+    assert st_ == pa.PA_OK and n == ws(960)
+    assert size(8, 32, 946, 257) == (pa.PA_OK, ws(1632))
+    assert size(8, 32, 1714, 257) == (pa.PA_OK, 0)    # 256-token chunk: 928 items, not split
+    assert size(8, 32, 10578, 257) == (pa.PA_OK, 0)   # whole prompts
+    assert size(8, 32, 498, 96) == (pa.PA_OK, 0)      # 48 key tiles: one piece
+    assert size(0, 32, 0, 4) == (pa.PA_OK, 0)
+    assert size(8, 31, 498, 257)[0] == pa.PA_ERR_INVALID_ARGUMENT  # 31 % 8 != 0
+    assert size(-1, 32, 498, 257)[0] == pa.PA_ERR_INVALID_ARGUMENT
+    assert lib.pa_prefill_split_workspace_size(ctypes.byref(d), 8, 32, 498, 257, None) \
+        == pa.PA_ERR_INVALID_ARGUMENT
+
+    p16 = ctypes.c_void_p(1 << 20)
+
+    def call(ws=p16, nbytes=n, T=498, maxb=257, q=p16):
+        return lib.pa_prefill_split(q, p16, p16, p16, maxb, p16, p16, 8, T, 16, 1.0, p16, 32,
+                                    ctypes.byref(d), ws, nbytes, None)
+
+    assert call(ws=None) == pa.PA_ERR_INVALID_ARGUMENT and b"workspace" in lib.pa_last_error()
+    assert call(nbytes=n - 1) == pa.PA_ERR_INVALID_ARGUMENT and b"needed" in lib.pa_last_error()
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == pa.PA_ERR_INVALID_ARGUMENT
+    assert call(q=None) == pa.PA_ERR_INVALID_ARGUMENT and b"NULL" in lib.pa_last_error()
+    assert call(T=0, q=None, ws=None) == pa.PA_OK  # nothing to do
+
+
 # ------------------------------------------------------------- allocator
 class _OOB(Exception):
     pass

@@ -243,3 +243,105 @@ def test_rising_logits_rescale_inside_the_key_loop():
 def test_f16_pools(G, H_kv, D, bs, lengths, nq):
     """The same causal attention on IEEE fp16 pools (fp16 MFMA operands)."""
     _check(91 + D + bs, lengths, nq, G=G, H_kv=H_kv, D=D, bs=bs, dtype="f16")
+
+
+# ---------------------------------------------------------------- split
+def _run_split(q, k, v, tables, lens, qs, bs, scale, dtype="bf16", reps=1):
+    """pa_prefill_split on NaN-filled outputs; with reps > 1 the same
+    workspace serves every call and each output must be identical."""
+    import torch
+    import paged_kv_cache_338_amd as pa
+    dev = "cuda:0"
+    qd = _bf16(q, dev, dtype)
+    kd, vd = _bf16(k, dev, dtype), _bf16(v, dev, dtype)
+    td, ld, qsd = (torch.from_numpy(x).to(dev) for x in (tables, lens, qs))
+    ws = pa.prefill_split_workspace(kd, len(lens), q.shape[1], q.shape[0], tables.shape[1])
+    res = None
+    for _ in range(reps):
+        out = torch.full_like(qd, float("nan"))
+        pa.pa_prefill_split(qd, kd, vd, td, ld, qsd, bs, scale, out, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().to(torch.float64).numpy()
+        if res is not None:
+            assert np.array_equal(got, res)
+        res = got
+    return res
+
+
+def _check_split(seed, lengths, nq, dtype="bf16", **kw):
+    q, k, v, t, lens, qs, bs = _case(seed, lengths, nq, dtype=dtype, **kw)
+    scale = 1.0 / np.sqrt(q.shape[2])
+    got = _run_split(q, k, v, t, lens, qs, bs, scale, dtype, reps=2)
+    want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, dtype)
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - want).max()) if got.size else 0.0
+    assert err <= TOL[dtype], err
+    return got
+
+
+@pytest.mark.parametrize("key_tiles", ["1", "3"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"G{s[0]}_H{s[1]}_D{s[2]}_bs{s[3]}" for s in SHAPES])
+def test_split_shapes(shape, key_tiles, monkeypatch):
+    """Every shape of the unsplit test with the key range cut into pieces of
+    1 or 3 key tiles (32 or 96 keys): pieces whose keys a row does not see
+    (before its causal limit) must drop out of the merge, and the last piece
+    of a block is short."""
+    monkeypatch.setenv("PA_PREFILL_KEY_TILES", key_tiles)
+    G, H_kv, D, bs, lengths, nq = shape
+    _check_split(sum(lengths) + G + 7, lengths, nq, G=G, H_kv=H_kv, D=D, bs=bs)
+
+
+def test_split_llama_shape_chunk64():
+    """The worked batch's last 64 tokens per sequence with the default plan
+    (pieces of 48 key tiles: the 4,100-token sequence's query blocks in 3
+    pieces), against the oracle and against the unsplit kernel."""
+    lengths = list(W.LLAMA3_8B_BATCH)
+    nq = [min(64, L) for L in lengths]
+    q, k, v, t, lens, qs, bs = _case(11, lengths, nq, G=4, H_kv=8, D=128, bs=16, spare=0)
+    scale = 1.0 / np.sqrt(128)
+    got = _run_split(q, k, v, t, lens, qs, bs, scale, reps=2)
+    want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "bf16")
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - want).max()) <= TOL["bf16"]
+    whole = _run(q, k, v, t, lens, qs, bs, scale)
+    assert float(np.abs(got - whole).max()) <= TOL["bf16"]
+
+
+def test_split_rising_logits(monkeypatch):
+    """Logits rising along the keys: every later piece has a larger reference
+    maximum than the earlier ones, so the merge must rescale each piece by
+    2^(m_i - M) (pieces of 2 key tiles)."""
+    monkeypatch.setenv("PA_PREFILL_KEY_TILES", "2")
+    lengths, nq = [700, 333], [30, 33]
+    q, k, v, t, lens, qs, bs = _case(78, lengths, nq, G=4, H_kv=2, D=128)
+    q[:] = W.round_to_bf16_bits(np.full(q.shape, 0.125, np.float32))
+    for b, L in enumerate(lengths):
+        for p in range(L):
+            k[t[b, p // bs], :, p % bs] = W.round_to_bf16_bits(np.full((2, 128), 0.05 * p, np.float32))
+    scale = 1.0 / np.sqrt(128)
+    got = _run_split(q, k, v, t, lens, qs, bs, scale)
+    want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "bf16")
+    assert float(np.abs(got - want).max()) <= TOL["bf16"]
+
+
+def test_split_f16_and_negative_scale(monkeypatch):
+    monkeypatch.setenv("PA_PREFILL_KEY_TILES", "2")
+    q, k, v, t, lens, qs, bs = _case(79, [300, 90, 5], [40, 90, 5], G=8, H_kv=1, D=64, bs=8,
+                                     dtype="f16")
+    for scale in (1.0 / 8, -1.0 / 8):
+        got = _run_split(q, k, v, t, lens, qs, bs, scale, "f16")
+        want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "f16")
+        assert float(np.abs(got - want).max()) <= TOL["f16"]
+
+
+def test_split_not_taken_for_many_query_blocks():
+    """With enough query blocks pa_prefill_split runs exactly as pa_prefill
+    (no workspace needed): bit-identical outputs."""
+    import paged_kv_cache_338_amd as pa
+    lengths = [256, 250, 256, 241, 256, 256, 199, 256]
+    q, k, v, t, lens, qs, bs = _case(80, lengths, lengths, G=4, H_kv=8, D=128)
+    d = pa.CacheDesc(k.shape[0], bs, 8, 128, pa.PA_BF16)
+    assert pa.pa_prefill_split_workspace_size(d, 8, 32, int(qs[-1]), t.shape[1]) == 0
+    a = _run(q, k, v, t, lens, qs, bs, 0.09)
+    b = _run_split(q, k, v, t, lens, qs, bs, 0.09)
+    assert np.array_equal(a, b)
