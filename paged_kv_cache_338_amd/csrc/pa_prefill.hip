@@ -118,6 +118,17 @@ struct TileGeo {
   static_assert(kLoads >= 1 && kKT * kPPR % kThreads == 0, "tile must split over the threads");
 };
 
+// ds_read_b64_tr_b16 (gfx950): 64 bits per lane from an LDS address, returned
+// transposed within each 16-lane row (lane i gets element i % 4 of the four
+// 16-bit values at lane 4e + i / 4's address, e = 0..3).  p must point into
+// LDS, 8-byte aligned.
+__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(uint2, x);
+}
+
 // Largest r in [0, B) with P[r] * H <= f (P: exclusive prefix sums in LDS).
 __device__ __forceinline__ int32_t find_item_seq(const int32_t* P, int32_t B, int32_t H,
                                                  int32_t f) {
@@ -370,7 +381,7 @@ prefill_kernel(PrefillArgs a) {
   //  ref[r]: lane 16j + c: reference max of row c (log2 units); thr[r] the
   //  raw score above which a logit exceeds ref[r] + 8;
   //  l[r], acc[r][blk]: lane 16j + c, register q: row 4j + q; acc at
-  //  column kBlk * c + blk.
+  //  column 16 blk + c.
   float ref[R], thr[R];
   floatx4_t l[R];
   floatx4_t acc[R][kBlk];
@@ -391,7 +402,7 @@ prefill_kernel(PrefillArgs a) {
   // front also reads the tile's V words (vw) right after the QK MFMAs, so
   // their LDS latency overlaps the softmax.
   floatx4_t s[2][R];
-  uint32_t vw[2][4][kBlk / 2];  // V rows 16 kb + 4j + q, columns kBlk*c ..
+  uint2 vt[kBlk][2];  // V[16 kb + 4j + e][16 blk + c], e = 0..3, as 4 16-bit values
   auto front = [&](int stage, int32_t t0, bool masked) __attribute__((always_inline)) -> bool {
     const char* Kl = tiles + stage * Geo::kStage;
     const char* Vl = Kl + Geo::kMat;
@@ -414,21 +425,19 @@ prefill_kernel(PrefillArgs a) {
           s[kb][r] = pa::mfma_k32<E>(kf[kb][ds], qf[r][ds], s[kb][r]);
       }
     }
+    // V through gfx950's transposing LDS read (ds_read_b64_tr_b16): within
+    // each 16-lane row j, lane i receives element i % 4 of the 4 16-bit
+    // values that lane 4e + i / 4 points at, e = 0..3.  Lane 16j + s points
+    // at key 4j + s / 4, columns 16 blk + 4 (s % 4) .. + 3, so lane 16j + c
+    // receives V[4j + e][16 blk + c]: the MFMA operand of column c over the
+    // keys 4j .. 4j + 3 (kb = 0) or 16 + 4j .. (kb = 1), in P's key order.
+    {
+      const char* vsrc = Vl + (4 * jr + (c16 >> 2)) * Geo::kRowLds + (c16 & 3) * 8;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int k = 0; k < kBlk; ++k)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const char* vp = Vl + (kb * 16 + 4 * jr + q) * Geo::kRowLds + c16 * (kBlk * 2);
-        if constexpr (kBlk == 8) {
-          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) vw[kb][q][w] = x[w];
-        } else {
-          const uint2 x = *reinterpret_cast<const uint2*>(vp);
-          vw[kb][q][0] = x.x;
-          vw[kb][q][1] = x.y;
-        }
-      }
+        for (int kb = 0; kb < 2; ++kb)
+          vt[k][kb] = lds_read_tr16(vsrc + kb * 16 * Geo::kRowLds + k * 32);
     }
     if (masked) {
 #pragma unroll
@@ -486,16 +495,11 @@ prefill_kernel(PrefillArgs a) {
       }
       l[r] = pa::mfma_k32<E>(pp[r], ones, l[r]);
     }
-    // For column group blk the lane's operand is V[key][kBlk*c+blk] over
-    // its 8 keys, in P's key order.
+    // For column block blk the lane's operand is V[key][16 blk + c] over its
+    // 8 keys, in P's key order, as the transposing reads left it.
 #pragma unroll
     for (int k = 0; k < kBlk; ++k) {
-      const int w = k >> 1;
-      const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
-      const u32x4_t vb = {__builtin_amdgcn_perm(vw[0][1][w], vw[0][0][w], sel),
-                          __builtin_amdgcn_perm(vw[0][3][w], vw[0][2][w], sel),
-                          __builtin_amdgcn_perm(vw[1][1][w], vw[1][0][w], sel),
-                          __builtin_amdgcn_perm(vw[1][3][w], vw[1][2][w], sel)};
+      const u32x4_t vb = {vt[k][0].x, vt[k][0].y, vt[k][1].x, vt[k][1].y};
 #pragma unroll
       for (int r = 0; r < R; ++r)
         acc[r][k] = pa::mfma_k32<E>(pp[r], vb, acc[r][k]);
@@ -600,11 +604,9 @@ prefill_kernel(PrefillArgs a) {
         const float refq = pa::pick_row_quad<q>(ref[0], jr);  // row 4j + q
         const int32_t ti = w0 + row / GP, g = row % GP;
         if (ti < w1 && g < G) {
-          floatx4_t* o = reinterpret_cast<floatx4_t*>(a.ws_o + (base + row) * D + kBlk * c16);
+          float* o = a.ws_o + (base + row) * D + c16;
 #pragma unroll
-          for (int k = 0; k < kBlk / 4; ++k)
-            o[k] = floatx4_t{acc[0][4 * k][q], acc[0][4 * k + 1][q], acc[0][4 * k + 2][q],
-                             acc[0][4 * k + 3][q]};
+          for (int k = 0; k < kBlk; ++k) o[16 * k] = acc[0][k][q];
           if (c16 == 0)
             *reinterpret_cast<f32x2_t*>(a.ws_ml + (base + row) * 2) = f32x2_t{refq, l[0][q]};
         }
@@ -620,15 +622,15 @@ prefill_kernel(PrefillArgs a) {
       const int32_t ti = w0 + r * TP + row / GP, g = row % GP;
       if (ti < w1 && g < G) {
         const float inv = 1.f / l[r][q];
-        uint32_t pk[kBlk / 2];
+        uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) +
+                        ((int64_t)(it.qs + ti) * H_q + kvh * G + g) * D + c16;
 #pragma unroll
         for (int k = 0; k < kBlk / 2; ++k) {
-          pk[k] = pa::pack2<E>(acc[r][2 * k][q] * inv, acc[r][2 * k + 1][q] * inv);
+          // columns 32 k + c and 32 k + 16 + c (lanes c of a row: 32 bytes each)
+          const uint32_t pk = pa::pack2<E>(acc[r][2 * k][q] * inv, acc[r][2 * k + 1][q] * inv);
+          dst[32 * k] = static_cast<uint16_t>(pk);
+          dst[32 * k + 16] = static_cast<uint16_t>(pk >> 16);
         }
-        char* dst = reinterpret_cast<char*>(a.out) +
-                    (((int64_t)(it.qs + ti) * H_q + kvh * G + g) * D + kBlk * c16) * 2;
-        if constexpr (kBlk == 8) *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
-        else *reinterpret_cast<uint2*>(dst) = uint2{pk[0], pk[1]};
       }
     });
   }
