@@ -57,6 +57,9 @@ constexpr int kOcc = 2;         // waves per SIMD the registers are sized for
 #ifndef PA_PREFILL_PD1
 #define PA_PREFILL_PD1 4  // tiles of loads in flight with one row block per wave
 #endif
+#ifndef PA_PREFILL_ROW_PAD
+#define PA_PREFILL_ROW_PAD 32  // bytes of padding per LDS row (build-time tuning knob)
+#endif
 #ifndef PA_PREFILL_PD2
 #define PA_PREFILL_PD2 2  // ... with two (its registers hold two)
 #endif
@@ -105,10 +108,11 @@ struct PrefillArgs {
 template <int D>
 struct TileGeo {
   static constexpr int kRowBytes = D * 2;
-  // LDS rows padded by 32 bytes: of the paddings measured (16, 32, 64
-  // bytes, 1.5x) the one with the fewest bank-conflict cycles (with 64)
-  // and the least LDS.
-  static constexpr int kRowLds = kRowBytes + 32;
+  // LDS rows padded by PA_PREFILL_ROW_PAD bytes (a multiple of 16).  With
+  // the K rows read 16 bytes per lane and V by transposing reads, 32 bytes
+  // is the fastest of 16, 32, 48 and 64 on the worked batch (whole prompts
+  // 298 us against 304-305 us).
+  static constexpr int kRowLds = kRowBytes + PA_PREFILL_ROW_PAD;
   static constexpr int kMat = kKT * kRowLds;           // one K or V tile in LDS
   static constexpr int kStage = 2 * kMat;              // K then V
   static constexpr int kPPR = kRowBytes / 16;          // 16-byte pieces per row
