@@ -34,6 +34,7 @@ one-thread passes of this batch and of the tiny reference batch.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -991,21 +992,25 @@ def main():
         step(i)
     torch.cuda.synchronize()
     kv_read.clear()
-    t_start = time.perf_counter()
     sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    gc.collect()
+    gc.disable()  # no collector pauses inside the timed steps
+    t_start = time.perf_counter()
     sev[0].record(stream)
     for i in range(args.warmup, total_steps):
         step(i)
         sev[i - args.warmup + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    gc.enable()
     gpu_ms = sev[0].elapsed_time(sev[-1])
     ms_step = max(gpu_ms, wall * 1e3) / args.steps
     step_ms = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)])
     sp10, sp50, sp90 = (float(x) for x in np.percentile(step_ms, [10, 50, 90]))
     value = sum(kv_read) / (ms_step * args.steps * 1e-3) / 1e9
     log(f"steps: {ms_step:.3f} ms/step ({ms_step * 1e3 / nl:.2f} us/layer; median {sp50:.3f}, "
-        f"p10 {sp10:.3f}, p90 {sp90:.3f} ms), {value:.0f} GB/s")
+        f"p10 {sp10:.3f}, p90 {sp90:.3f}, max {step_ms.max():.3f} ms; wall {wall * 1e3:.1f} ms, "
+        f"GPU {gpu_ms:.1f} ms), {value:.0f} GB/s")
 
     mode = "eager launches" if args.eager else "HIP graph replay of the layer loop"
     result = {
@@ -1021,7 +1026,7 @@ def main():
                    "tokens_added_per_step": B, "layers": nl,
                    "us_per_layer": round(ms_step * 1e3 / nl, 3),
                    "step_ms_median": round(sp50, 4), "step_ms_p10": round(sp10, 4),
-                   "step_ms_p90": round(sp90, 4)},
+                   "step_ms_p90": round(sp90, 4), "step_ms_max": round(float(step_ms.max()), 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
