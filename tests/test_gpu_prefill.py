@@ -345,3 +345,53 @@ def test_split_not_taken_for_many_query_blocks():
     a = _run(q, k, v, t, lens, qs, bs, 0.09)
     b = _run_split(q, k, v, t, lens, qs, bs, 0.09)
     assert np.array_equal(a, b)
+
+
+# ------------------------------------------------- full size, sampled rows
+def _sampled_rows_match(got, q, k, v, t, lens, qs, bs, scale, per_seq, seed):
+    """Row (b, i) of a prefill is the decode of sequence b cut at its
+    position L_b - n_b + i, with that row's query: the oracle's decode
+    (pinned on its own) recomputes a sample of rows, every head."""
+    from oracle import attention as oatt
+    rng = np.random.default_rng(seed)
+    rows, pos, seq = [], [], []
+    for b in range(len(lens)):
+        n = int(qs[b + 1] - qs[b])
+        if n == 0:
+            continue
+        pick = {0, n - 1} | set(int(x) for x in rng.integers(0, n, per_seq))
+        for i in sorted(pick):
+            rows.append(int(qs[b]) + i)
+            pos.append(int(lens[b]) - n + i)
+            seq.append(b)
+    want = oatt.paged_decode(q[rows], k, v, t[seq], np.array(pos) + 1, bs, scale, "bf16")
+    err = float(np.abs(got[rows] - want).max())
+    assert err <= TOL["bf16"], err
+    return len(rows)
+
+
+def test_full_worked_batch_whole_prompts_sampled():
+    """The prefill bench's workload at full size: the worked batch's 10,578
+    prompt tokens as queries, 32 query / 8 KV heads, head 128, bs 16 (the
+    two-row-block kernel).  Every output finite; 8 sampled rows per sequence
+    plus its first and last, all 32 heads, against the oracle's decode."""
+    lengths = list(W.LLAMA3_8B_BATCH)
+    q, k, v, t, lens, qs, bs = _case(21, lengths, lengths, G=4, H_kv=8, D=128, bs=16, spare=0)
+    scale = 1.0 / np.sqrt(128)
+    got = _run(q, k, v, t, lens, qs, bs, scale)
+    assert np.isfinite(got).all()
+    assert _sampled_rows_match(got, q, k, v, t, lens, qs, bs, scale, 8, 22) >= 16
+
+
+@pytest.mark.parametrize("chunk", [512, 128, 64])
+def test_full_worked_batch_chunks_sampled(chunk):
+    """The chunked-prefill bench workloads at full size through
+    pa_prefill_split with its default plan (the 64- and 128-token chunks are
+    split along the keys, the 512-token chunk is not)."""
+    lengths = list(W.LLAMA3_8B_BATCH)
+    nq = [min(chunk, L) for L in lengths]
+    q, k, v, t, lens, qs, bs = _case(23 + chunk, lengths, nq, G=4, H_kv=8, D=128, bs=16, spare=0)
+    scale = 1.0 / np.sqrt(128)
+    got = _run_split(q, k, v, t, lens, qs, bs, scale)
+    assert np.isfinite(got).all()
+    assert _sampled_rows_match(got, q, k, v, t, lens, qs, bs, scale, 8, 24 + chunk) >= 16
