@@ -200,6 +200,20 @@ def cpu_baseline(w, seconds):
                       f"in {el:.1f} s, NumPy fp64 paged decode incl. bf16 widening"}
 
 
+def copy_calibration(mib):
+    """4 device copies of mib MiB (the runtime's copy kernel): a plain copy of
+    known size, to scale the HBM byte counters of a profiler pass."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 4 copies of {n} bytes")
+
+
 def copy_bandwidth(dev, nbytes=1 << 30, reps=5):
     """A 1 GiB device-to-device copy (torch copy_), timed with HIP events:
     the bandwidth a plain copy reaches on this GPU, beside the decode's."""
@@ -840,6 +854,8 @@ def main():
             cache_ops_workload(args)
         else:
             other_workload(args)
+        if args.copy_calibration > 0:
+            copy_calibration(args.copy_calibration)
         return
     import torch
 
@@ -1048,13 +1064,7 @@ def main():
     result["roofline"]["copy_1gib"] = cb
     log(f"1 GiB device copy: {cb['read_plus_write_GBps']:.0f} GB/s read + write")
     if args.copy_calibration > 0:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy calibration: 4 copies of {n} bytes")
+        copy_calibration(args.copy_calibration)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)...")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
