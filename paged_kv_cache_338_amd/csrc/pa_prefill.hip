@@ -14,19 +14,26 @@
 // Work decomposition: a workgroup takes one (sequence, KV head, query
 // block): 4 waves x R row blocks x 16 rows, a row being one (query token,
 // head of the KV head's group) pair, GP heads per token (G rounded up to a
-// power of two; rows of heads >= G are padding).  Query blocks of a sequence
-// are ordered longest first.  The workgroup walks the keys of its causal
-// range in tiles of 32: the 256 threads gather a tile's K and V rows through
-// the block table into registers (one tile ahead, with the table entries
-// read one tile earlier still), store them to a double-buffered, padded LDS
-// tile, and every wave then computes its rows against it.  So each K/V byte
-// crosses the cache hierarchy once per 64 R rows, not once per 16.
+// power of two; rows of heads >= G are padding).  Items go longest first:
+// sequences by length (for batches of up to 256), each one's query blocks
+// from the last.  The workgroup walks the keys of its causal range in tiles
+// of 32: the 256 threads gather a tile's K and V rows through the block
+// table into registers (tiles ahead, with the table entries read one tile
+// earlier still), store them to a double-buffered, padded LDS tile, and
+// every wave then computes its rows against it.  So each K/V byte crosses
+// the cache hierarchy once per 64 R rows, not once per 16.
 //
-// Per tile and row block, on the MFMA units (v_mfma_f32_16x16x32_bf16
-// throughout): S = K Q^T (two 16-key blocks), the lazily rescaled online
-// softmax of the decode kernel, then O += P V and l += P 1 with the 32 keys
-// as the contraction.  Only the tiles that cross a wave's first diagonal
-// mask anything; K/V rows past the cache length are loaded as zeros.
+// Per tile and row block, on the MFMA units (v_mfma_f32_16x16x32, bf16 or
+// fp16): S = K Q^T (two 16-key blocks), the lazily rescaled online softmax
+// of the decode kernel, then O += P V and l += P 1 with the 32 keys as the
+// contraction, V read from LDS by transposing reads straight into the
+// operand layout.  Only the tiles that cross a wave's first diagonal mask
+// anything; K/V rows past the cache length are loaded as zeros.
+//
+// pa_prefill_split, for calls with few query blocks: each query block's key
+// range is cut into pieces of key tiles, one workgroup per piece, which
+// leaves per row (reference maximum, sum, unnormalised output) in a
+// workspace; a second kernel merges a block's pieces.
 //
 // The query rows are MFMA operands in the pool's 16-bit format, so the call
 // takes bf16 or fp16 pools.
