@@ -179,6 +179,51 @@ def test_shapes(shape):
     assert_close(w, gc.decode(tables=wide, lens=lo), oc.decode())
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_batch_of_8192_sequences(dtype):
+    """The largest batch pa_decode takes (8,192 sequences): its lengths
+    snapshot needs more than 64 KiB of LDS (the launch raises the kernel's
+    LDS limit), and the merge grid has 8,192 x H_kv x G workgroups.  Lengths
+    0..40 (some empty), one KV head, head 64, 16-token blocks, blocks
+    shuffled over the pool; every other slot NaN.  Tables and pools are
+    built directly (the allocator's own tests cover the allocator)."""
+    import torch
+    import paged_kv_cache_338_amd as pa
+    B, H_kv, G, D, bs = 8192, 1, 4, 64, 16
+    rng = np.random.default_rng(8192 + (dtype == "f32"))
+    lens = rng.integers(0, 41, B).astype(np.int32)
+    nblk = -(-lens // bs)
+    nb = int(nblk.sum()) + 1
+    perm = rng.permutation(nb).astype(np.int32)
+    maxb = int(nblk.max())
+    tables = np.full((B, maxb), -1, np.int32)
+    starts = np.concatenate([[0], np.cumsum(nblk)])
+    for b in range(B):
+        tables[b, :nblk[b]] = perm[starts[b]:starts[b + 1]]
+    seq = np.repeat(np.arange(B), lens)
+    pos = np.concatenate([np.arange(L) for L in lens])
+    blk, off = tables[seq, pos // bs], pos % bs
+    store = np.uint16 if dtype == "bf16" else np.float32
+    poison = np.array(0x7FC0, np.uint16) if dtype == "bf16" else np.float32(np.nan)
+    k = np.full((nb, H_kv, bs, D), poison, store)
+    v = np.full((nb, H_kv, bs, D), poison, store)
+    k[blk, :, off] = W._normal(rng, (len(seq), H_kv, D), dtype)
+    v[blk, :, off] = W._normal(rng, (len(seq), H_kv, D), dtype)
+    q = W._normal(rng, (B, G * H_kv, D), dtype)
+    scale = 1.0 / np.sqrt(D)
+    want = oatt.paged_decode(q, k, v, tables, lens, bs, scale, dtype)
+    gd, dev = _gd(), "cuda:0"
+    qd = gd.to_torch(q, dtype, dev)
+    out = torch.empty_like(qd)
+    pa.pa_decode(qd, gd.to_torch(k, dtype, dev), gd.to_torch(v, dtype, dev),
+                 torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), bs, scale, out)
+    torch.cuda.synchronize()
+    got = gd.widen_out(out, dtype)
+    assert np.isfinite(got).all()
+    assert np.array_equal(got[lens == 0], np.zeros_like(got[lens == 0]))
+    assert float(np.abs(got - want).max()) <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_single_token_returns_v_exactly(dtype):
     w = _small(5, [1, 1, 1], G=4, H_kv=2, D=128, bs=16, dtype=dtype)

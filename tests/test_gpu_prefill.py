@@ -186,6 +186,17 @@ def test_batches_at_the_ranking_limit(B):
     _check(B + 5, lengths, nq, G=4, H_kv=1, D=64, bs=16, spare=0)
 
 
+def test_maximum_batch_of_8192_sequences():
+    """The largest batch pa_prefill takes: 8,192 short prompts (0..24 tokens,
+    some with no queries), so the per-sequence snapshot needs about 98 KiB
+    of LDS (the launch raises the kernel's limit) and batch order is kept
+    (more than 256 sequences)."""
+    rng = np.random.default_rng(4096)
+    lengths = [int(x) for x in rng.integers(1, 25, 8192)]
+    nq = [int(min(L, x)) for L, x in zip(lengths, rng.integers(0, 25, 8192))]
+    _check(8191, lengths, nq, G=4, H_kv=1, D=64, bs=16, spare=0)
+
+
 def test_rejects_f32_pools_and_bad_arguments():
     import torch
     import paged_kv_cache_338_amd as pa
