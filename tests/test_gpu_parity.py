@@ -179,24 +179,17 @@ def test_shapes(shape):
     assert_close(w, gc.decode(tables=wide, lens=lo), oc.decode())
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_maximum_batch_of_8192_sequences(dtype):
-    """The largest batch pa_decode takes (8,192 sequences): its lengths
-    snapshot needs more than 64 KiB of LDS (the launch raises the kernel's
-    LDS limit), and the merge grid has 8,192 x H_kv x G workgroups.  Lengths
-    0..40 (some empty), one KV head, head 64, 16-token blocks, blocks
-    shuffled over the pool; every other slot NaN.  Tables and pools are
-    built directly (the allocator's own tests cover the allocator)."""
-    import torch
-    import paged_kv_cache_338_amd as pa
-    B, H_kv, G, D, bs = 8192, 1, 4, 64, 16
-    rng = np.random.default_rng(8192 + (dtype == "f32"))
-    lens = rng.integers(0, 41, B).astype(np.int32)
+def _direct_case(seed, lens, H_kv, G, D, bs, dtype):
+    """Pools, tables and queries built directly: each sequence's blocks a
+    shuffled slice of the pool, only its own token slots hold values, every
+    other slot NaN."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, np.int32)
+    B = len(lens)
     nblk = -(-lens // bs)
     nb = int(nblk.sum()) + 1
     perm = rng.permutation(nb).astype(np.int32)
-    maxb = int(nblk.max())
-    tables = np.full((B, maxb), -1, np.int32)
+    tables = np.full((B, max(1, int(nblk.max()))), -1, np.int32)
     starts = np.concatenate([[0], np.cumsum(nblk)])
     for b in range(B):
         tables[b, :nblk[b]] = perm[starts[b]:starts[b + 1]]
@@ -210,15 +203,47 @@ def test_maximum_batch_of_8192_sequences(dtype):
     k[blk, :, off] = W._normal(rng, (len(seq), H_kv, D), dtype)
     v[blk, :, off] = W._normal(rng, (len(seq), H_kv, D), dtype)
     q = W._normal(rng, (B, G * H_kv, D), dtype)
-    scale = 1.0 / np.sqrt(D)
-    want = oatt.paged_decode(q, k, v, tables, lens, bs, scale, dtype)
+    return q, k, v, tables, lens
+
+
+def _direct_decode(q, k, v, tables, lens, bs, scale, dtype):
+    import torch
+    import paged_kv_cache_338_amd as pa
     gd, dev = _gd(), "cuda:0"
     qd = gd.to_torch(q, dtype, dev)
     out = torch.empty_like(qd)
     pa.pa_decode(qd, gd.to_torch(k, dtype, dev), gd.to_torch(v, dtype, dev),
                  torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), bs, scale, out)
     torch.cuda.synchronize()
-    got = gd.widen_out(out, dtype)
+    return gd.widen_out(out, dtype)
+
+
+def test_one_context_of_131072_tokens():
+    """One 131,072-token sequence beside two short ones, 8 query / 2 KV heads,
+    head 128: each of its two segments spans about 500 of the grid's 1,024
+    waves, so the merge combines more contributors than one pass holds."""
+    q, k, v, tables, lens = _direct_case(131072, [131072, 3, 700], 2, 4, 128, 16, "bf16")
+    scale = 1.0 / np.sqrt(128)
+    got = _direct_decode(q, k, v, tables, lens, 16, scale, "bf16")
+    want = oatt.paged_decode(q, k, v, tables, lens, 16, scale, "bf16")
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - want).max()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_batch_of_8192_sequences(dtype):
+    """The largest batch pa_decode takes (8,192 sequences): its lengths
+    snapshot needs more than 64 KiB of LDS (the launch raises the kernel's
+    LDS limit), and the merge grid has 8,192 x H_kv x G workgroups.  Lengths
+    0..40 (some empty), one KV head, head 64, 16-token blocks, blocks
+    shuffled over the pool; every other slot NaN.  Tables and pools are
+    built directly (the allocator's own tests cover the allocator)."""
+    rng = np.random.default_rng(8192 + (dtype == "f32"))
+    lens = rng.integers(0, 41, 8192).astype(np.int32)
+    q, k, v, tables, lens = _direct_case(8192 + (dtype == "f32"), lens, 1, 4, 64, 16, dtype)
+    scale = 1.0 / 8
+    want = oatt.paged_decode(q, k, v, tables, lens, 16, scale, dtype)
+    got = _direct_decode(q, k, v, tables, lens, 16, scale, dtype)
     assert np.isfinite(got).all()
     assert np.array_equal(got[lens == 0], np.zeros_like(got[lens == 0]))
     assert float(np.abs(got - want).max()) <= TOL[dtype]

@@ -406,3 +406,16 @@ def test_full_worked_batch_chunks_sampled(chunk):
     got = _run_split(q, k, v, t, lens, qs, bs, scale)
     assert np.isfinite(got).all()
     assert _sampled_rows_match(got, q, k, v, t, lens, qs, bs, scale, 8, 24 + chunk) >= 16
+
+
+def test_split_chunk_against_131072_token_context():
+    """A 64-token chunk at the end of a 131,072-token context (plus two short
+    prompts): the default plan cuts its query blocks' 4,096 key tiles into 64
+    pieces of 64 tiles (the grid bound of 24 items times 64 pieces stays at
+    1,536 workgroups), so the merge combines 64 partial states per row."""
+    lengths, nq = [131072, 40, 300], [64, 40, 30]
+    q, k, v, t, lens, qs, bs = _case(131, lengths, nq, G=4, H_kv=2, D=128, bs=16, spare=0)
+    scale = 1.0 / np.sqrt(128)
+    got = _run_split(q, k, v, t, lens, qs, bs, scale)
+    assert np.isfinite(got).all()
+    assert _sampled_rows_match(got, q, k, v, t, lens, qs, bs, scale, 12, 132) >= 6
