@@ -419,3 +419,71 @@ def test_split_chunk_against_131072_token_context():
     got = _run_split(q, k, v, t, lens, qs, bs, scale)
     assert np.isfinite(got).all()
     assert _sampled_rows_match(got, q, k, v, t, lens, qs, bs, scale, 12, 132) >= 6
+
+
+def test_split_graph_replay_matches_eager():
+    """pa_prefill_split enqueues only its two kernels (no memset, no
+    allocation), so it can be captured in a HIP graph.  The graph is replayed
+    four times with eager split calls on the same workspace and
+    synchronisations in between, and the query starts changed before one
+    replay (the kernels read them at run time); every replay must equal the
+    eager result bit for bit."""
+    import torch
+    import paged_kv_cache_338_amd as pa
+    lengths, nq = [900, 4100, 60, 1500], [64, 64, 60, 64]
+    q, k, v, t, lens, qs, bs = _case(301, lengths, nq, G=4, H_kv=2, D=128, bs=16, spare=0)
+    scale = 1.0 / np.sqrt(128)
+    dev = "cuda:0"
+    qd = _bf16(q, dev)
+    kd, vd = _bf16(k, dev), _bf16(v, dev)
+    td, ld, qsd = (torch.from_numpy(x).to(dev) for x in (t, lens, qs))
+    ws = pa.prefill_split_workspace(kd, len(lens), q.shape[1], q.shape[0], t.shape[1])
+    assert ws.numel() > 256  # this shape is split
+    call = lambda out: pa.pa_prefill_split(qd, kd, vd, td, ld, qsd, bs, scale, out, workspace=ws)
+    out_e = torch.full_like(qd, float("nan"))
+    call(out_e)
+    torch.cuda.synchronize()
+    want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "bf16")
+    assert float(np.abs(out_e.cpu().to(torch.float64).numpy() - want).max()) <= TOL["bf16"]
+    # The same rows with the second sequence's chunk cut to its last 20 tokens.
+    qs2 = qs.copy()
+    qs2[2:] -= 44
+    nq2 = [64, 20, 60, 64]
+    q2 = np.concatenate([q[:64], q[64 + 44:128], q[128:]])
+    out_e2 = torch.full_like(qd, float("nan"))
+    qsd.copy_(torch.from_numpy(qs2))
+    pa.pa_prefill_split(_bf16(q2, dev), kd, vd, td, ld, qsd, bs, scale, out_e2[:int(qs2[-1])],
+                        workspace=ws)
+    torch.cuda.synchronize()
+    qsd.copy_(torch.from_numpy(qs))
+    out_g = torch.empty_like(qd)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out_g)  # eager first: library loaded, attributes set
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            call(out_g)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        cut = rep == 2
+        qsd.copy_(torch.from_numpy(qs2 if cut else qs))
+        if cut:
+            qd[:int(qs2[-1])].copy_(_bf16(q2, dev))
+        else:
+            qd.copy_(_bf16(q, dev))
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = out_e2[:int(qs2[-1])] if cut else out_e
+        got = out_g[:int(qs2[-1])] if cut else out_g
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), rep
+        # eager work on the same workspace between replays
+        scratch = torch.full_like(qd, float("nan"))
+        qsd.copy_(torch.from_numpy(qs))
+        qd.copy_(_bf16(q, dev))
+        call(scratch)
+        torch.cuda.synchronize()
+        assert torch.equal(scratch.view(torch.int16), out_e.view(torch.int16))
