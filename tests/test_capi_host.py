@@ -162,6 +162,55 @@ def test_prefill_split_plan_on_the_host():
     assert call(T=0, q=None, ws=None) == pa.PA_OK  # nothing to do
 
 
+def test_prefill_split_grid_bounds_the_pieces():
+    """For random batches (query counts summing to T, lengths >= query counts,
+    tables wide enough), the pieces the split kernel enumerates never exceed
+    the grid implied by pa_prefill_split_workspace_size: per sequence and KV
+    head, query blocks of QT = 64 / GP tokens from the start, block qb seeing
+    keys 0 .. L - n + min((qb + 1) QT, n) - 1, cut into ceil(tiles / kt)
+    pieces.  The grid is workspace // (256 (D + 2)) (64 rows of D + 2 floats
+    per piece, two 256-byte-aligned regions); kt is not exported, but the
+    grid's pieces per item S fix kt >= ceil(max tiles / S), and fewer key
+    tiles per piece only make more pieces, so that kt bounds them all."""
+    lib = pa.load_library()
+    rng = np.random.default_rng(2024)
+    checked = 0
+    for _ in range(400):
+        G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        H_kv = int(rng.integers(1, 9))
+        D = int(rng.choice([64, 128]))
+        bs = int(rng.choice([1, 4, 16, 32, 128]))
+        B = int(rng.integers(1, 40))
+        L = rng.integers(1, 20000, B)
+        n = np.minimum(L, rng.integers(0, 80, B))
+        T = int(n.sum())
+        if T == 0:
+            continue
+        maxb = int(-(-L.max() // bs)) + int(rng.integers(0, 3))
+        d = pa.CacheDesc(1 << 20, bs, H_kv, D, pa.PA_BF16)
+        ws = ctypes.c_size_t(0)
+        assert lib.pa_prefill_split_workspace_size(ctypes.byref(d), B, G * H_kv, T, maxb,
+                                                   ctypes.byref(ws)) == pa.PA_OK
+        if ws.value == 0:
+            continue
+        GP = 1 << (G - 1).bit_length()
+        QT = 4 * (16 // GP)
+        items1 = ((T + QT - 1) // QT + B) * H_kv
+        grid = ws.value // (256 * (D + 2))
+        assert grid % items1 == 0, (grid, items1)
+        S = grid // items1
+        maxtiles = -(-(maxb * bs) // 32)
+        kt = -(-maxtiles // S)
+        pieces = 0
+        for Lb, nb in zip(L.tolist(), n.tolist()):
+            for qb in range(-(-nb // QT)):
+                tiles = (Lb - nb + min((qb + 1) * QT, nb) - 1) // 32 + 1
+                pieces += -(-tiles // kt) * H_kv
+        assert pieces <= grid, (pieces, grid, B, T, maxb, bs, G, H_kv)
+        checked += 1
+    assert checked >= 50
+
+
 # ------------------------------------------------------------- allocator
 class _OOB(Exception):
     pass
