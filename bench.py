@@ -70,7 +70,8 @@ def parse():
                         "of known size, to scale the HBM byte counters of a profiler pass)")
     p.add_argument("--workload", default="llama3_8b_decode",
                    help="llama3_8b_decode (the default bench line), or serving_batch, "
-                        "block_size_sweep_bs{8,16,32,128}, prefix_sharing_p{2056,2048}: pa_decode "
+                        "block_size_sweep_bs{8,16,32,128}, prefix_sharing_p{2056,2048}, "
+                        "worked_batch_xN (the worked batch repeated N times): pa_decode "
                         "alone on that workload's batch (kernel leg only); llama3_8b_prefill, "
                         "llama3_8b_chunked_prefill_cN: pa_prefill alone on the worked batch; "
                         "swap_llama3_8b: pa_swap_blocks out to pinned host memory and back; "
@@ -297,6 +298,12 @@ def other_workload(args):
         name = name[:-len("_f16")]
     if name == "llama3_8b_decode":
         w = W.llama3_8b_decode(with_values=False)
+    elif name.startswith("worked_batch_x"):
+        # The worked batch repeated N times (8N sequences, pool 4096N blocks):
+        # how the fixed costs of a call fade as the batch grows.
+        n = int(name[len("worked_batch_x"):])
+        w = W.llama3_8b_decode(lengths=list(W.LLAMA3_8B_BATCH) * n, num_blocks=4096 * n,
+                               with_values=False)
     elif name.startswith("block_size_sweep_bs"):
         w = W.block_size_sweep(int(name[len("block_size_sweep_bs"):]), with_values=False)
     elif name.startswith("prefix_sharing_p"):
