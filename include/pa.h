@@ -381,6 +381,13 @@ int32_t pa_allocator_num_cached(const pa_allocator* alloc);
 pa_status pa_allocator_cached_list(const pa_allocator* alloc, int32_t* out, int32_t cap,
                                    int32_t* len);
 
+/* Whether block `block` holds a prefix-cache key (in use or evictable), and
+ * that key (0 when it holds none or the cache is off).  For bit-exact
+ * comparisons of the cache's state.  INVALID_ARGUMENT for a block outside
+ * the pool. */
+pa_status pa_block_prefix_key(const pa_allocator* alloc, int32_t block, int32_t* cached_out,
+                              uint64_t* key_out);
+
 /* *out = 1 if seq_id is swapped out, else 0. */
 pa_status pa_seq_is_swapped(const pa_allocator* alloc, int64_t seq_id, int32_t* out);
 /* Free host blocks (-1 without a host pool), and the host stack, the block

@@ -17,7 +17,10 @@ import os
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+# PA_LIBRARY may name another build of the same library (the sanitized host
+# build, libpa_sanitize.so); it must exist like the default one.
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_OK = 0
 PA_ERR_INVALID_ARGUMENT = 1
@@ -99,6 +102,7 @@ SIGNATURES = {
     "pa_seq_match_prefix": (_I32, [_P, _I64, _PI32, _I32, _PI32]),
     "pa_allocator_num_cached": (_I32, [_P]),
     "pa_allocator_cached_list": (_I32, [_P, _PI32, _I32, _PI32]),
+    "pa_block_prefix_key": (_I32, [_P, _I32, _PI32, _c.POINTER(_c.c_uint64)]),
 }
 
 _lib = None
@@ -282,6 +286,10 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale
     maxb = block_tables.shape[1]
     if workspace is None:
         workspace = decode_workspace(k_cache, B, H_q, maxb)
+        if stream is not None and stream != torch.cuda.current_stream():
+            # The temporary is freed on return: keep the caching allocator
+            # from reusing it before the kernels on `stream` are done.
+            workspace.record_stream(stream)
     _check(load_library().pa_decode(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_tables, "block_tables"), maxb, _dev(context_lens, "context_lens"), B,
@@ -330,6 +338,8 @@ def pa_prefill_split(q, k_cache, v_cache, block_tables, context_lens, query_star
     if workspace is None:
         workspace = prefill_split_workspace(k_cache, context_lens.numel(), q.shape[1], q.shape[0],
                                             block_tables.shape[1])
+        if stream is not None and stream != _torch().cuda.current_stream():
+            workspace.record_stream(stream)
     prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size,
                     scale, out, stream, workspace=workspace)()
     return out
@@ -511,6 +521,13 @@ class Allocator:
         _check(self._lib.pa_allocator_cached_list(self._h, _ptr(out, ctypes.c_int32), out.size,
                                                   ctypes.byref(ln)))
         return out[:ln.value].tolist()
+
+    def block_key(self, block):
+        """The prefix-cache key a block holds, or None."""
+        c = ctypes.c_int32(0)
+        k = ctypes.c_uint64(0)
+        _check(self._lib.pa_block_prefix_key(self._h, int(block), ctypes.byref(c), ctypes.byref(k)))
+        return k.value if c.value else None
 
     def seq_is_swapped(self, seq_id):
         v = ctypes.c_int32(0)

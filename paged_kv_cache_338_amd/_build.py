@@ -1,6 +1,22 @@
 """Builds libpa.so in-tree: host C++ with g++, device code with hipcc (gfx950).
 
 Run as ``python -m paged_kv_cache_338_amd._build``.  Always recompiles.
+
+``python -m paged_kv_cache_338_amd._build --sanitize`` builds a second copy,
+``libpa_sanitize.so``, whose host sources (the allocator and the status
+calls) are compiled by g++ with AddressSanitizer and UndefinedBehavior-
+Sanitizer and linked by g++; the device sources are built as usual (the
+sanitizers cover host code only).  The binding loads it when PA_LIBRARY
+names it; the CPU tests of the allocator then run under the sanitizers
+with the two runtimes preloaded:
+
+    PA_LIBRARY=$PWD/paged_kv_cache_338_amd/libpa_sanitize.so \
+    LD_PRELOAD="$(g++ -print-file-name=libasan.so):$(g++ -print-file-name=libubsan.so)" \
+    ASAN_OPTIONS=detect_leaks=0 UBSAN_OPTIONS=halt_on_error=1:print_stacktrace=1 \
+    python -m pytest tests/test_capi_host.py -q -p no:cacheprovider
+
+(leak checking is off because the Python interpreter itself keeps
+allocations until exit).
 """
 
 from __future__ import annotations
@@ -16,6 +32,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
+SANITIZE_LIB = os.path.join(PKG, "libpa_sanitize.so")
 
 ARCH = "gfx950"
 HOST_SOURCES = ["pa_status.cpp", "pa_allocator.cpp"]
@@ -25,6 +42,8 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wall", "-Wno-unused-command-line-argument"]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+# Host-only instrumentation for the --sanitize copy (g++ lines only).
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g"]
 
 
 def _hipcc():
@@ -45,25 +64,54 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
+def _device_objects(verbose):
+    hipcc = _hipcc()
+    objs = []
+    for src in DEVICE_SOURCES:
+        obj = os.path.join(OBJ, src + ".o")
+        _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    return objs
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    hipcc = _hipcc()
     cxx = shutil.which("g++") or "g++"
     objs = []
     for src in HOST_SOURCES:
         obj = os.path.join(OBJ, src + ".o")
         _run([cxx, *CXX_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
-    for src in DEVICE_SOURCES:
-        obj = os.path.join(OBJ, src + ".o")
-        _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+    objs += _device_objects(verbose)
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    _run([_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
 
+def build_sanitize(verbose: bool = True) -> str:
+    """libpa_sanitize.so: sanitized host objects (g++), plain device objects,
+    linked by g++ against the HIP runtime."""
+    os.makedirs(OBJ, exist_ok=True)
+    cxx = shutil.which("g++") or "g++"
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(OBJ, src + ".san.o")
+        _run([cxx, *CXX_FLAGS, *SANITIZE_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src),
+              "-o", obj], verbose)
+        objs.append(obj)
+    objs += _device_objects(verbose)
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    tmp = SANITIZE_LIB + ".tmp"
+    _run([cxx, "-shared", *SANITIZE_FLAGS, *objs, "-L", rocm_lib, f"-Wl,-rpath,{rocm_lib}",
+          "-lamdhip64", "-o", tmp], verbose)
+    os.replace(tmp, SANITIZE_LIB)
+    return SANITIZE_LIB
+
+
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv)
-    print(LIB)
+    if "--sanitize" in sys.argv:
+        print(build_sanitize(verbose="-q" not in sys.argv))
+    else:
+        build(verbose="-q" not in sys.argv)
+        print(LIB)

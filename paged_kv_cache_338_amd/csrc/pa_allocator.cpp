@@ -81,8 +81,8 @@ struct Undo {
   enum Kind : uint8_t { kPop, kRefcount, kTableAppend, kTableSet, kTokens, kEvict,
                         kRegister } kind;
   Sequence* seq;
-  int32_t a;  // block (kPop, kRefcount), logical index (kTableSet)
-  int32_t b;  // old value (kRefcount, kTableSet, kTokens)
+  int32_t a;  // block (kPop, kRefcount, kEvict, kRegister), logical index (kTableSet)
+  int32_t b;  // old value (kRefcount, kTableSet, kTokens); saved key index (kRegister)
 };
 
 }  // namespace
@@ -94,6 +94,10 @@ struct pa_allocator {
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, Sequence> seqs;
   std::vector<Undo> undo;  // reused between calls
+  // Keys a kRegister overwrote, restored by the rollback: an evicted block
+  // that the same call refills and registers under a new key must get its
+  // old key back before the eviction itself is undone.
+  std::vector<BlockKey> saved_keys;
   bool has_host = false;
   int32_t num_host_blocks = 0;
   std::vector<int32_t> host_free;  // top at back()
@@ -132,10 +136,12 @@ struct pa_allocator {
         case Undo::kRegister:
           cached[it->a] = 0;
           block_of.erase(bkey[it->a].key);
+          bkey[it->a] = std::move(saved_keys[it->b]);
           break;
       }
     }
     undo.clear();
+    saved_keys.clear();
   }
 
   bool pop(int32_t* blk) {
@@ -178,10 +184,11 @@ struct pa_allocator {
     const BlockKey& k = s->keys[lb];
     if (block_of.count(k.key)) return;
     const int32_t blk = s->table[lb];
+    undo.push_back({Undo::kRegister, nullptr, blk, static_cast<int32_t>(saved_keys.size())});
+    saved_keys.push_back(std::move(bkey[blk]));
     bkey[blk] = k;
     cached[blk] = 1;
     block_of[k.key] = blk;
-    undo.push_back({Undo::kRegister, nullptr, blk, 0});
   }
 
   void set_refcount(int32_t blk, int32_t value) {
@@ -301,6 +308,7 @@ pa_status pa_seq_reserve(pa_allocator* alloc, const int64_t* seq_ids, const int3
 
   const int32_t bs = alloc->block_size;
   alloc->undo.clear();
+  alloc->saved_keys.clear();
   int32_t pairs = 0;
   int64_t t = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -347,6 +355,7 @@ pa_status pa_seq_reserve(pa_allocator* alloc, const int64_t* seq_ids, const int3
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "%d copy pairs > cow_cap = %d", pairs, cow_cap);
   }
   alloc->undo.clear();
+  alloc->saved_keys.clear();
   if (num_cow_out) *num_cow_out = pairs;
   return PA_OK;
 }
@@ -523,6 +532,18 @@ pa_status pa_allocator_cached_list(const pa_allocator* alloc, int32_t* out, int3
   if (cap < nc) return pa::fail(PA_ERR_INVALID_ARGUMENT, "cap %d < %d cached blocks", cap, nc);
   if (nc > 0 && !out) return pa::fail(PA_ERR_INVALID_ARGUMENT, "out is NULL");
   std::copy(alloc->lru.begin(), alloc->lru.end(), out);
+  return PA_OK;
+}
+
+pa_status pa_block_prefix_key(const pa_allocator* alloc, int32_t block, int32_t* cached_out,
+                              uint64_t* key_out) {
+  if (!alloc || !cached_out || !key_out)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (block < 0 || block >= alloc->num_blocks)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "block %d outside [0, %d)", block, alloc->num_blocks);
+  const bool c = alloc->prefix_cache && alloc->cached[block];
+  *cached_out = c ? 1 : 0;
+  *key_out = c ? alloc->bkey[block].key : 0;
   return PA_OK;
 }
 

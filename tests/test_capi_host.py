@@ -390,6 +390,8 @@ class LockstepMachine(RuleBasedStateMachine):
         assert _state(self.o, self.N) == _state(self.c, self.N)
         assert self.o.host_free_list() == self.c.host_free_list()
         assert self.o.cached_list() == self.c.cached_list()
+        assert [self.o.block_key(b) for b in range(self.N)] == \
+            [self.c.block_key(b) for b in range(self.N)]
         for s in self.o.seq_ids():
             assert self.o.seq_block_table(s) == self.c.seq_block_table(s)
             assert self.o.seq_num_tokens(s) == self.c.seq_num_tokens(s)
@@ -444,6 +446,8 @@ def test_workload_scripts_bit_exact(name, make):
     assert np.array_equal(np.array(lens_o), lens_c)
     assert np.array_equal(lens_c, w.context_lens)
     assert o.free_list() == c.free_list()
+    assert [o.refcount(b) for b in range(w.num_blocks)] == \
+        [c.refcount(b) for b in range(w.num_blocks)]
     if name == "prefix2056":
         assert len(lc[-1][1]) == 127
     if name == "prefix2048":

@@ -129,6 +129,31 @@ def check_rollback_keeps_cache(cls):
     assert a.match_prefix(1, list(range(12)) + [5]) == 12
 
 
+def check_failed_reserve_keeps_evicted_keys(cls):
+    """A reserve that evicts a cached block, refills it (registering a new
+    key on it) and then runs out of blocks must give the block its old key
+    back: afterwards the old prompt still hits and the new one does not."""
+    a = cls(1, 2)
+    a.enable_prefix_cache()
+    a.seq_create(0)
+    assert a.match_prefix(0, [1, 2, 3]) == 0
+    a.seq_reserve([0], [2])  # block 0 full: cached under the key of [1, 2]
+    a.seq_free(0)
+    assert a.cached_list() == [0] and a.block_key(0) == block_key(0, [1, 2])
+    a.seq_create(1)
+    assert a.match_prefix(1, [5, 6, 7]) == 0
+    with pytest.raises(OutOfBlocks):
+        a.seq_reserve([1], [3])  # evicts block 0, fills it with [5, 6], needs a 2nd
+    assert a.cached_list() == [0] and a.num_free() == 0
+    assert a.block_key(0) == block_key(0, [1, 2])
+    a.seq_free(1)
+    a.seq_create(2)
+    assert a.match_prefix(2, [5, 6, 7]) == 0
+    a.seq_free(2)
+    a.seq_create(3)
+    assert a.match_prefix(3, [1, 2, 3]) == 2 and a.seq_block_table(3) == [0]
+
+
 def check_errors(cls):
     a = cls(8, BS)
     a.seq_create(0)
@@ -141,7 +166,8 @@ def check_errors(cls):
 
 
 PREFIX_PINS = [check_repeat_hits, check_one_token_left, check_chained_keys, check_live_sharing,
-               check_free_first_then_lru, check_rollback_keeps_cache, check_errors]
+               check_free_first_then_lru, check_rollback_keeps_cache,
+               check_failed_reserve_keeps_evicted_keys, check_errors]
 
 
 @pytest.mark.parametrize("pin", PREFIX_PINS, ids=lambda f: f.__name__)
