@@ -96,6 +96,21 @@ const char* pa_last_error(void);
  * otherwise. */
 pa_status pa_supported(const pa_cache_desc* desc, int32_t num_q_heads);
 
+/* Process-wide tuning knobs.  Each changes only how work is spread over
+ * the GPU, never the result beyond fp32 summation order; 0 (the default)
+ * lets the library choose.  Read by every later call of the operation
+ * (atomically; any thread may set them).
+ *   PA_TUNE_DECODE_WORKGROUPS: workgroups of pa_decode's grid, in
+ *     [1, 1024] (default 256, one per compute unit).
+ *   PA_TUNE_PREFILL_KEY_TILES: key tiles of 32 keys per piece when
+ *     pa_prefill_split splits (default: from the shape, at least 48).
+ * INVALID_ARGUMENT for an unknown key or a value out of range. */
+typedef int32_t pa_tuning_key;
+#define PA_TUNE_DECODE_WORKGROUPS 1
+#define PA_TUNE_PREFILL_KEY_TILES 2
+pa_status pa_set_tuning(pa_tuning_key key, int32_t value);
+pa_status pa_get_tuning(pa_tuning_key key, int32_t* value);
+
 /* ---------------------------------------------------------------- device */
 
 /* Slot-mapped append [P3 Step 4: each decode step writes the new token's
@@ -165,15 +180,21 @@ pa_status pa_swap_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, const 
  * block_size:   must equal desc->block_size.
  * out:          device [num_seqs][num_q_heads][head_dim], pool dtype.
  * workspace:    device scratch of at least pa_decode_workspace_size() bytes,
- *               256-byte aligned, needing no initialisation.  The call owns
- *               it until the stream reaches the end of the call; calls that
- *               share a workspace must be ordered (one stream, or events).
+ *               256-byte aligned, ZERO-FILLED before its first use (for
+ *               instance by hipMemset or torch.zeros); every call leaves it
+ *               ready for the next one (its arrival counters back at zero),
+ *               so one zero fill serves any number of calls, graph replays
+ *               included.  The call owns it until the stream reaches the end
+ *               of the call; calls that share a workspace must be ordered
+ *               (one stream, or events): overlapping calls race.
  * num_seqs:     at most 8192 (PA_ERR_UNSUPPORTED beyond, or when the lengths
- *               snapshot and merge buffers would not fit in LDS).
- * The work is split over the grid in equal shares of (sequence, KV head,
- * 16-token tile) units.  A sequence cut by a share boundary leaves partial
- * results in the workspace, merged by a second small kernel launched on the
- * same stream by the same call. */
+ *               snapshot would not fit in LDS); num_kv_heads at most 4096.
+ * One kernel launch.  The (KV head, sequence, 16-token tile) units are split
+ * over the grid in equal shares, dealt so that each XCD takes consecutive
+ * shares.  A sequence cut by a share boundary leaves partial results (max,
+ * sum, unnormalised output) in the workspace; the last workgroup to finish
+ * a piece of it merges them (out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M)
+ * l_i, M = max_i m_i), so no workgroup waits for another. */
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* context_lens, int32_t num_seqs, int32_t block_size,

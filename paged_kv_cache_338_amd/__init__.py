@@ -31,6 +31,8 @@ PA_ERR_DEVICE = 5
 PA_F32 = 0
 PA_BF16 = 1
 PA_F16 = 2
+PA_TUNE_DECODE_WORKGROUPS = 1
+PA_TUNE_PREFILL_KEY_TILES = 2
 
 STATUS_NAMES = {PA_ERR_INVALID_ARGUMENT: "INVALID_ARGUMENT", PA_ERR_OUT_OF_BLOCKS: "OUT_OF_BLOCKS",
                 PA_ERR_UNKNOWN_SEQ: "UNKNOWN_SEQ", PA_ERR_UNSUPPORTED: "UNSUPPORTED",
@@ -65,6 +67,8 @@ _PDESC = _c.POINTER(CacheDesc)
 # name -> (restype, argtypes); mirrors include/pa.h
 SIGNATURES = {
     "pa_abi_version": (_I32, []),
+    "pa_set_tuning": (_I32, [_I32, _I32]),
+    "pa_get_tuning": (_I32, [_I32, _PI32]),
     "pa_status_string": (_c.c_char_p, [_I32]),
     "pa_last_error": (_c.c_char_p, []),
     "pa_supported": (_I32, [_PDESC, _I32]),
@@ -185,6 +189,32 @@ def _same_pool(k_cache, v_cache):
         raise ValueError("k_cache and v_cache must have the same shape and dtype")
 
 
+def pa_set_tuning(key, value):
+    """Sets a process-wide tuning knob (0 = the library's choice)."""
+    _check(load_library().pa_set_tuning(int(key), int(value)))
+
+
+def pa_get_tuning(key):
+    v = ctypes.c_int32(0)
+    _check(load_library().pa_get_tuning(int(key), ctypes.byref(v)))
+    return v.value
+
+
+class tuning:
+    """Context manager: sets a tuning knob and restores its previous value."""
+
+    def __init__(self, key, value):
+        self.key, self.value = key, value
+
+    def __enter__(self):
+        self.old = pa_get_tuning(self.key)
+        pa_set_tuning(self.key, self.value)
+        return self
+
+    def __exit__(self, *exc):
+        pa_set_tuning(self.key, self.old)
+
+
 def pa_supported(desc, num_q_heads):
     return load_library().pa_supported(ctypes.byref(desc), num_q_heads) == PA_OK
 
@@ -260,11 +290,12 @@ def pa_decode_workspace_size(desc, num_seqs, num_q_heads, max_blocks_per_seq):
 
 
 def decode_workspace(k_cache, num_seqs, num_q_heads, max_blocks_per_seq):
-    """Allocates (with torch) a workspace sized for pa_decode.  It needs no
-    initialisation, and one workspace serves any number of ordered calls."""
+    """Allocates (with torch) a zero-filled workspace sized for pa_decode; one
+    workspace serves any number of ordered calls (each leaves it ready for
+    the next)."""
     torch = _torch()
     n = pa_decode_workspace_size(cache_desc(k_cache), num_seqs, num_q_heads, max_blocks_per_seq)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=k_cache.device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=k_cache.device)
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,

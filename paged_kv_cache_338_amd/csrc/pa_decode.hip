@@ -1,5 +1,5 @@
 // Single-query (decode) attention that reads K/V through per-sequence block
-// tables (gfx950 / CDNA4, wave64).
+// tables (gfx950 / CDNA4, wave64), in one kernel launch.
 //
 // Sources: "Paged Attention" (klaylearn.com glossary), body: the kernel
 // turns a token position into (logical block, offset), looks the physical
@@ -10,39 +10,51 @@
 // attention arithmetic itself is unchanged by paging.
 //
 // Work decomposition:
-//  * A segment is one (sequence b, KV head) pair; it has ceil(L_b / 16)
-//    tiles of 16 tokens.  All tiles of all segments are numbered in one flat
-//    order (b, KV head, tile).  Wave w of the W waves of the grid takes the
-//    equal share [T*w/W, T*(w+1)/W) of the T tiles, so every wave streams
-//    the same number of K/V bytes whatever the length mix, and no wave ever
-//    waits for another.
-//  * Each workgroup first copies the context lengths into LDS with their
-//    prefix sums over sequences, so its waves see one consistent snapshot.
-//  * Blocks of >= 16 tokens: a wave walks its share as batches of up to
+//  * A segment is one (KV head, sequence b) pair; it has ceil(L_b / 16)
+//    tiles of 16 tokens.  All tiles are numbered in one flat, head-major
+//    order (KV head, b, tile).  The T tiles are cut into equal shares, one
+//    per workgroup, and each workgroup's share into equal sub-shares, one
+//    per wave, so every wave streams the same number of K/V bytes whatever
+//    the length mix.
+//  * The dispatcher deals workgroups to the 8 XCDs in turn, so workgroups
+//    blockIdx and blockIdx + 8 run on the same XCD (which XCD takes
+//    blockIdx 0 varies from launch to launch).  Shares are therefore dealt
+//    by blockIdx % 8 first: the workgroups of one XCD take consecutive
+//    shares, and with a multiple of 8 KV heads every XCD owns whole heads,
+//    so every segment's pieces are computed on one XCD.  Correctness does
+//    not depend on this placement (see below); only the merge's speed does.
+//  * Blocks of >= 16 tokens: a wave walks its sub-share as batches of up to
 //    NBUF tiles; a batch holds the rest of one segment and, if that segment
 //    ends inside it, the start of the next, so crossing a segment boundary
-//    costs no extra round trip.  The block ids of the share are fetched 64
-//    tiles at a time by one vector load (lane i: tile i) and read with
-//    v_readlane a batch ahead; each batch issues its segments' query rows
-//    and all its tile loads before the first use.  Smaller blocks: one
-//    pipelined piece per segment, block ids gathered per lane.
-//  * A segment wholly inside the share is written out by the wave; a piece
-//    of a segment cut by a share boundary leaves its online-softmax state
-//    (max, sum, unnormalised output) as a partial in the workspace.
-//  * A second, small kernel merges the partials of each cut segment (the
-//    wave that holds a segment's first tile writes the segment's record), so
-//    there is no cross-wave synchronisation inside the decode kernel: on
-//    this part, publishing data to other workgroups inside one kernel costs
-//    far more (an L2 writeback per release) than a second launch.
-//  * Per tile (bf16 pools): the K rows of the 16 tokens are the A operand of
-//    a v_mfma_f32_16x16x32_bf16 chain whose B operand is the KV head's G
-//    query rows, so the logits of head g and token 4j+r land in lane 16j+g,
-//    register r.  The probabilities, rounded to bf16, are the A operand of
-//    a v_mfma_f32_16x16x16_bf16 chain against the V rows (D/16 output
-//    column blocks) and against a ones operand (the softmax sums), so the
-//    output and its normaliser accumulate in MFMA registers.
-//    fp32 pools use v_mfma_f32_16x16x4_f32 for the logits and the VALU for
-//    P*V, with the probabilities broadcast by DPP.
+//    costs no extra round trip.  The block ids of the sub-share are fetched
+//    64 tiles at a time by one vector load (lane i: tile i) and read with
+//    v_readlane a batch ahead; each batch issues its segments' query rows and
+//    all its tile loads before the first use.  Smaller blocks: one pipelined
+//    piece per segment, block ids gathered per lane.
+//  * A segment wholly inside a wave's sub-share is written out by the wave.
+//    A piece cut by a sub-share boundary leaves its online-softmax state
+//    (max, sum, unnormalised output) in LDS; after a barrier the workgroup
+//    combines the pieces of each segment, writes the segments that lie
+//    inside its share and publishes one partial state for each segment cut
+//    by its share boundary (at most two).
+//  * Cut segments are merged inside the kernel by the last workgroup to
+//    publish a piece (a per-segment arrival counter; no workgroup ever waits
+//    for another).  Pieces are published with device-scope stores, and the
+//    counter also sums the XCD numbers of the contributors (and their
+//    squares), read from the hardware.  When all of them ran on the
+//    merger's XCD, every piece went through its L2 and is read from there;
+//    otherwise the merger reads at device scope.  The merger restores the
+//    counter to zero, so a zero-filled workspace stays ready for the next
+//    call (graph replays included).
+//  * Per tile (bf16 / fp16 pools): the K rows of the 16 tokens are the A
+//    operand of a v_mfma_f32_16x16x32 chain whose B operand is the KV head's
+//    G query rows, so the logits of head g and token 4j+r land in lane
+//    16j+g, register r.  The probabilities, rounded to the pool's 16-bit
+//    format, are the A operand of a v_mfma_f32_16x16x16 chain against the V
+//    rows (D/16 output column blocks) and against a ones operand (the
+//    softmax sums), so the output and its normaliser accumulate in MFMA
+//    registers.  fp32 pools use v_mfma_f32_16x16x4_f32 for the logits and
+//    the VALU for P*V, with the probabilities broadcast by DPP.
 //  * The running max is raised lazily: only when a logit exceeds it by more
 //    than 8 (log2 units) are the sum and output rescaled, so most tiles skip
 //    the rescale.  Any reference value gives the same softmax.
@@ -57,7 +69,6 @@
 
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
 #include <type_traits>
 
 #include "pa_attn_tile.h"
@@ -66,8 +77,8 @@
 
 namespace {
 
-using pa::bf16x8_t;
 using pa::f32x2_t;
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 using pa::floatx4_t;
 using pa::Geometry;
 using pa::issue_tile;
@@ -75,28 +86,22 @@ using pa::issue_tile_small;
 using pa::kTile;
 using pa::kWave;
 using pa::MfmaState;
-using pa::s16x4_t;
 using pa::TileRegs;
 using pa::u32x4_t;
 using pa::uni;
-using pa::uniform_ptr;
-constexpr int kMaxWaves = 4096;   // the workspace holds partials for this many waves
-constexpr int kDefaultWGs = 256;  // workgroups of the decode grid
+constexpr int kMaxWGs = 1024;     // grid bound: the workspace holds 2 pieces per workgroup
+constexpr int kDefaultWGs = 256;  // one workgroup per compute unit
+constexpr int kXcds = 8;          // XCDs of the part; workgroups are dealt to them in turn
 constexpr int kMaxSeqs = 8192;    // lengths snapshot in LDS
-constexpr int kRecInts = 8;       // ints per segment record
-constexpr int kMergeWG = 256;     // threads of the partial-merge kernel
+constexpr int kMaxKvHeads = 4096; // a segment's (sequence, KV head) packs into 32 bits
+constexpr int kNW = 4;            // waves per workgroup
+constexpr int kWG = kNW * kWave;
+constexpr int kSlots = 2 * kNW;   // LDS piece slots: two per wave
 constexpr size_t kMaxLds = 160 * 1024;
-#ifndef PA_DECODE_NW
-#define PA_DECODE_NW 4  // waves per workgroup
-#endif
-#ifndef PA_DECODE_OCC_STREAM
-#define PA_DECODE_OCC_STREAM 2  // waves per SIMD the streamed bf16 path's registers must allow
-#endif
-#ifndef PA_DECODE_OCC
-#define PA_DECODE_OCC 2  // waves per SIMD the register budget must allow
-#endif
+// Cache-policy operand of the buffer intrinsics: device scope (sc1).
+constexpr int kDeviceScope = 16;
 #ifndef PA_DECODE_NB_BF16
-#define PA_DECODE_NB_BF16 3  // tiles per batch for bf16 pools (build-time tuning knob)
+#define PA_DECODE_NB_BF16 3  // tiles per batch for 16-bit pools (build-time tuning knob)
 #endif
 
 struct DecodeArgs {
@@ -106,10 +111,10 @@ struct DecodeArgs {
   const int32_t* tables;
   const int32_t* lens;
   void* out;
-  float* ws_o;       // [2 * kMaxWaves][G][D] unnormalised partial outputs
-  float* ws_m;       // [2 * kMaxWaves][G] running max (log2 units)
-  float* ws_l;       // [2 * kMaxWaves][G] sum of exp2(x - max)
-  int32_t* records;  // [B * H_kv][kRecInts] per segment: cut? and its contributors
+  float* ws_o;        // [2 * kMaxWGs][G][D] published pieces: unnormalised output
+  float* ws_ml;       // [2 * kMaxWGs][G][2] their reference max (log2 units) and sum
+                      // of exp2(x - max), side by side so one 8-byte load fetches both
+  uint64_t* counters;  // [H_kv * B] arrival counters, zero between calls
   int32_t B;
   int32_t max_blocks;
   int32_t num_blocks;
@@ -138,33 +143,36 @@ struct WaveState {
   }
 };
 
-// One segment (sequence b, KV head kvh) and its flat tile range [S0, S1).
+// One segment (KV head kvh, sequence b) and its flat tile range [S0, S1).
 struct Seg {
   int32_t b, kvh, nt, L, S0, S1;
 };
 
-// Largest b in [0, B) with PB[b] * H_kv <= f (PB: exclusive prefix sums of
-// tiles per sequence, in LDS).
-__device__ __forceinline__ int32_t find_seq(const int32_t* PB, int32_t B, int32_t H_kv,
-                                            int32_t f) {
+// Largest b in [0, B) with PB[b] <= r (PB: exclusive prefix sums of tiles
+// per sequence, in LDS).  For r < PB[B] that is the non-empty sequence
+// holding tile r of a head.
+__device__ __forceinline__ int32_t find_seq(const int32_t* PB, int32_t B, int32_t r) {
   int32_t lo = 0, hi = B - 1;
   while (lo < hi) {
     const int32_t mid = (lo + hi + 1) >> 1;
-    if (PB[mid] * H_kv <= f) lo = mid;
+    if (PB[mid] <= r) lo = mid;
     else hi = mid - 1;
   }
   return lo;
 }
 
-// The segment holding flat tile f (0 <= f < total); f is wave-uniform.
+// The segment holding flat tile f (0 <= f < H_kv * NT, NT = tiles per head);
+// f is wave-uniform.
 __device__ __forceinline__ Seg seg_containing(const int32_t* PB, const int32_t* Ls, int32_t B,
-                                              int32_t H_kv, int32_t f) {
+                                              int32_t H_kv, int32_t NT, int32_t f) {
   Seg s;
-  s.b = uni(find_seq(PB, B, H_kv, f));
+  s.kvh = uni(min(static_cast<int32_t>(static_cast<uint32_t>(f) / static_cast<uint32_t>(NT)),
+                  H_kv - 1));
+  const int32_t r = f - s.kvh * NT;
+  s.b = uni(find_seq(PB, B, r));
   const int32_t pb = uni(PB[s.b]);
   s.nt = max(uni(PB[s.b + 1]) - pb, 1);
-  s.kvh = min((f - pb * H_kv) / s.nt, H_kv - 1);
-  s.S0 = pb * H_kv + s.kvh * s.nt;
+  s.S0 = s.kvh * NT + pb;
   s.S1 = s.S0 + s.nt;
   s.L = uni(Ls[s.b]);
   return s;
@@ -174,24 +182,25 @@ __device__ __forceinline__ Seg seg_containing(const int32_t* PB, const int32_t* 
 // one exists; should the snapshot say otherwise, s becomes an empty segment
 // at the end of every range, which stops every loop that walks segments.
 __device__ __forceinline__ void seg_advance(Seg& s, const int32_t* PB, const int32_t* Ls,
-                                            int32_t B, int32_t H_kv) {
-  if (s.kvh + 1 < H_kv) {
-    s.kvh += 1;
-    s.S0 = s.S1;
-    s.S1 += s.nt;
-    return;
-  }
+                                            int32_t B, int32_t H_kv, int32_t NT) {
+  // The next sequence with tiles, in this head or a later one (the empty
+  // sequences of a head are the same in every head).
   int32_t b = s.b + 1;
   while (b < B && uni(PB[b + 1]) == uni(PB[b])) ++b;
+  int32_t kvh = s.kvh;
   if (b >= B) {
-    s.S0 = s.S1 = 0x7FFFFFFF;
-    return;
+    b = 0;
+    while (b < B && uni(PB[b + 1]) == uni(PB[b])) ++b;
+    ++kvh;
   }
+  const bool end = kvh >= H_kv || b >= B;
+  b = min(b, B - 1);
+  const int32_t pb = uni(PB[b]);
   s.b = b;
-  s.kvh = 0;
-  s.S0 = uni(PB[b]) * H_kv;
-  s.nt = uni(PB[b + 1]) - uni(PB[b]);
-  s.S1 = s.S0 + s.nt;
+  s.kvh = kvh;
+  s.nt = uni(PB[b + 1]) - pb;
+  s.S0 = end ? 0x7FFFFFFF : kvh * NT + pb;
+  s.S1 = end ? 0x7FFFFFFF : s.S0 + s.nt;
   s.L = uni(Ls[b]);
 }
 
@@ -299,9 +308,17 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int32_t b, int32_t k
 }
 
 // Largest w with floor(T * w / W) <= f: the share (of W equal shares of T
-// units) that holds unit f, for 0 <= f < T.
+// units) that holds unit f, for 0 <= f < T < 2^31 and W <= 2^10, i.e.
+// floor(((f + 1) W - 1) / T).  The quotient comes from one double division
+// (its operands, below 2^41, are exact) and one integer check fixes the
+// rounding; a 64-bit integer division would be a long software sequence on
+// the critical path of the merge.
 __device__ __forceinline__ int32_t share_of(int32_t f, int32_t T, int32_t W) {
-  return static_cast<int32_t>((((int64_t)f + 1) * W - 1) / T);
+  const int64_t x = ((int64_t)f + 1) * W - 1;
+  int32_t w = static_cast<int32_t>(static_cast<double>(x) / static_cast<double>(T));
+  if ((int64_t)w * T > x) --w;
+  else if ((int64_t)(w + 1) * T <= x) ++w;
+  return w;
 }
 
 template <int E>
@@ -310,24 +327,57 @@ __device__ __forceinline__ void store_out(void* out, int64_t i, float x) {
   else reinterpret_cast<float*>(out)[i] = x;
 }
 
-template <int E, int D, int GP, int kNW, int NBUF, bool kSmall>
-__global__ void __launch_bounds__(kNW * kWave)
-__attribute__((amdgpu_waves_per_eu(kSmall ? (((E != 0) || GP * D < 16 * 128) ? PA_DECODE_OCC : 1)
-                                          : ((E != 0) ? PA_DECODE_OCC_STREAM : 1))))
+// Four output values of one head row, rounded once, stored with one write.
+template <int E>
+__device__ __forceinline__ void store_out4(void* out, int64_t i, floatx4_t x) {
+  if constexpr (E != 0) {
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + i) =
+        uint2{pa::pack2<E>(x[0], x[1]), pa::pack2<E>(x[2], x[3])};
+  } else {
+    *reinterpret_cast<floatx4_t*>(reinterpret_cast<float*>(out) + i) = x;
+  }
+}
+
+// XCD the running workgroup was placed on (hardware register XCC_ID, bits
+// 3:0).
+__device__ __forceinline__ int32_t xcd_id() {
+  return static_cast<int32_t>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xF);
+}
+
+// LDS of the workgroup step: one piece slot per (wave, end of its
+// sub-share) with its unnormalised output, reference max and sum, and the
+// slot's segment.
+template <int D, int GP>
+struct LdsPieces {
+  float o[kSlots][GP][D];
+  float m[kSlots][GP];
+  float l[kSlots][GP];
+  int4 seg[kSlots];        // S0, S1, b | kvh << 16 (kvh < 2^15), valid: one 16-byte read
+  int32_t flag[2];         // per published piece: 0 not last, 1 merge from L2, 2 at device scope
+};
+
+template <int E, int D, int GP, int NBUF, bool kSmall>
+__global__ void __launch_bounds__(kWG)
+__attribute__((amdgpu_waves_per_eu(kSmall ? (((E != 0) || GP * D < 16 * 128) ? 2 : 1)
+                                          : ((E != 0) ? 2 : 1))))
 decode_kernel(DecodeArgs a) {
   constexpr bool BF16 = E != 0;  // 16-bit pools (bf16 or fp16)
   using Geo = Geometry<BF16, D>;
-  constexpr int kWG = kNW * kWave;
+  using Pieces = LdsPieces<D, GP>;
+  constexpr int kC4 = D / 4;  // 4-column groups of a head row
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), v = tid >> 6;
   const int jr = lane >> 4, c16 = lane & 15;
-  const int32_t wg = blockIdx.x, nwg = gridDim.x;
+  const int32_t bx = blockIdx.x, nwg = gridDim.x;
   const int32_t B = a.B, H_kv = a.H_kv, G = a.G, H_q = H_kv * G;
 
-  // LDS: the lengths snapshot and its prefix sums.
-  int32_t* PB = reinterpret_cast<int32_t*>(smem);  // [B + 1]
-  int32_t* Ls = PB + B + 1;                        // [B]
-  int32_t* misc = Ls + B;                          // [kNW]
+  // LDS: the pieces, then the lengths snapshot and its prefix sums.
+  Pieces& P = *reinterpret_cast<Pieces*>(smem);
+  int32_t* PB = reinterpret_cast<int32_t*>(smem + sizeof(Pieces));  // [B + 1]
+  int32_t* Ls = PB + B + 1;                                          // [B]
+  int32_t* misc = Ls + B;                                            // [kNW]
+
+  if (lane < 2) P.seg[2 * v + lane] = int4{0, 0, 0, 0};
 
   // ---- lengths snapshot and prefix sums of tiles per sequence
   const int32_t len_cap = a.max_blocks << a.log2_bs;
@@ -358,55 +408,49 @@ decode_kernel(DecodeArgs a) {
   if (tid == 0) PB[B] = carry;
   __syncthreads();
 
-  const int32_t Tt = uni(PB[B]) * H_kv;  // flat tiles (host bounds it below 2^31)
+  const int32_t NT = uni(PB[B]);  // tiles per KV head
+  const int32_t Tt = NT * H_kv;   // flat tiles (host bounds it below 2^31)
 
   // Sequences with no context get a zero row (workgroup b % W writes it).
-  for (int32_t b = wg; b < B; b += nwg) {
+  for (int32_t b = bx; b < B; b += nwg) {
     if (Ls[b] == 0) {
       for (int32_t e = tid; e < H_q * D; e += kWG)
         store_out<E>(a.out, (int64_t)b * H_q * D + e, 0.f);
-      for (int32_t h = tid; h < H_kv; h += kWG) a.records[(b * H_kv + h) * kRecInts] = 0;
     }
   }
-  // ---- this wave's share [G0, G1): wave wv of Wt, the equal share
-  // [T*wv/Wt, T*(wv+1)/Wt) of the flat tiles.
-  const int32_t Wt = nwg * kNW, wv = wg * kNW + v;
-  // floor(Tt * w / Wt) in 32-bit arithmetic: Tt = qt * Wt + rt with rt < Wt
-  // <= 4096, so rt * w < 2^24 (64-bit division would cost hundreds of
-  // instructions on the critical path of every wave).
-  const uint32_t qt = static_cast<uint32_t>(Tt) / static_cast<uint32_t>(Wt);
-  const uint32_t rt = static_cast<uint32_t>(Tt) - qt * static_cast<uint32_t>(Wt);
+  if (Tt == 0) return;
+
+  // ---- shares.  Logical workgroup lw takes share [T*lw/W, T*(lw+1)/W);
+  // with W a multiple of 8 the workgroups with blockIdx = x mod 8 (one XCD)
+  // take the consecutive logical indices x*W/8 .. (x+1)*W/8 - 1.
+  const int32_t per_xcd = nwg % kXcds == 0 ? nwg / kXcds : 0;
+  const int32_t lw = per_xcd ? (bx % kXcds) * per_xcd + bx / kXcds : bx;
+  // floor(Tt * w / nwg) in 32-bit arithmetic: Tt = qt * nwg + rt with
+  // rt < nwg <= 1024, so rt * w < 2^21.
+  const uint32_t qt = static_cast<uint32_t>(Tt) / static_cast<uint32_t>(nwg);
+  const uint32_t rt = static_cast<uint32_t>(Tt) - qt * static_cast<uint32_t>(nwg);
   auto bound = [&](uint32_t w) {
-    return static_cast<int32_t>(qt * w + rt * w / static_cast<uint32_t>(Wt));
+    return static_cast<int32_t>(qt * w + rt * w / static_cast<uint32_t>(nwg));
   };
-  const int32_t G0 = uni(bound(wv)), G1 = uni(bound(wv + 1));
+  const int32_t A0 = uni(bound(lw)), A1 = uni(bound(lw + 1));
+  const int32_t G0 = uni(A0 + static_cast<int32_t>((int64_t)(A1 - A0) * v / kNW));
+  const int32_t G1 = uni(A0 + static_cast<int32_t>((int64_t)(A1 - A0) * (v + 1) / kNW));
   const int log2_bs = a.log2_bs;
   const int nbt = log2_bs >= 4 ? 1 : (kTile >> log2_bs);  // table lanes per tile
   const int tpc_log = log2_bs >= 4 ? 6 : 2 + log2_bs;       // log2(tiles per table chunk)
 
   using State = std::conditional_t<BF16, MfmaState<D>, WaveState<false, D, GP>>;
-  // Finishes segment s after its last tile in this share.  A segment wholly
-  // inside the share is written out; a cut piece leaves (max, sum,
-  // unnormalised output) in partial slot 2*wv + 0 if the segment began
-  // before the share, else 2*wv + 1.
+  // Finishes segment s after its last tile in this wave's sub-share.  A
+  // segment wholly inside the sub-share is written out; a cut piece leaves
+  // (max, sum, unnormalised output) in LDS slot 2v + 0 if the segment began
+  // before the sub-share, else 2v + 1.
   auto finish = [&](const State& st, const Seg s) {
     const bool whole = s.S0 >= G0 && s.S1 <= G1;
-    const int32_t pslot = 2 * wv + (s.S0 < G0 ? 0 : 1);
-    float* slot = a.ws_o + (int64_t)pslot * G * D;
-    if (s.S0 >= G0 && lane == 0) {
-      // This wave holds the segment's first tile: it writes the segment's
-      // record for the merge kernel (cut or not, tile range, decomposition).
-      int32_t* rec = a.records + (s.b * H_kv + s.kvh) * kRecInts;
-      rec[0] = whole ? 0 : 1;
-      rec[1] = s.S0;
-      rec[2] = s.S1;
-      rec[3] = Tt;
-      rec[4] = Wt;
-      rec[5] = wv;
-    }
+    const int slot = 2 * v + (s.S0 < G0 ? 0 : 1);
+    if (!whole && lane == 0) P.seg[slot] = int4{s.S0, s.S1, s.b | (s.kvh << 16), 1};
     if constexpr (BF16) {
-      // ---- finish the piece: sums over the 4 rows; the accumulators
-      // already hold whole tiles (lane 16j + c, register r: head 4j + r).
+      // The accumulators already hold whole tiles (lane 16j + c, register
+      // r: head 4j + r, columns kBlk*c .. kBlk*c + kBlk - 1).
       constexpr int kBlk = D / 16;
       pa::static_for<0, 4>([&](auto Q) {
         constexpr int q = decltype(Q)::value;
@@ -417,22 +461,23 @@ decode_kernel(DecodeArgs a) {
             const float inv = 1.f / lg;
             uint32_t pk[kBlk / 2];
 #pragma unroll
-            for (int i = 0; i < kBlk / 2; ++i) {
+            for (int i = 0; i < kBlk / 2; ++i)
               pk[i] = pa::pack2<E>(st.acc[2 * i][q] * inv, st.acc[2 * i + 1][q] * inv);
-            }
             char* dst = reinterpret_cast<char*>(a.out) +
                         ((((int64_t)s.b * H_kv + s.kvh) * G + g) * D + kBlk * c16) * 2;
             if constexpr (kBlk == 8) *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
             else *reinterpret_cast<uint2*>(dst) = uint2{pk[0], pk[1]};
           } else {
-            float* dst = slot + g * D + kBlk * c16;
+            float* dst = &P.o[slot][g][kBlk * c16];
 #pragma unroll
-            for (int i = 0; i < kBlk; ++i) dst[i] = st.acc[i][q];
+            for (int i = 0; i < kBlk; i += 4)
+              *reinterpret_cast<floatx4_t*>(dst + i) =
+                  floatx4_t{st.acc[i][q], st.acc[i + 1][q], st.acc[i + 2][q], st.acc[i + 3][q]};
+            if (c16 == 0) P.l[slot][g] = lg;
           }
         }
-        if (!whole && c16 == 0 && g < G) a.ws_l[pslot * G + g] = lg;
       });
-      if (!whole && lane < G) a.ws_m[pslot * G + lane] = st.ref;
+      if (!whole && lane < G) P.m[slot][lane] = st.ref;
     } else {
       // ---- merge the 4 row states (lanes g, 16+g, 32+g, 48+g hold head g)
       const float M = pa::rows_max(st.m);
@@ -444,9 +489,7 @@ decode_kernel(DecodeArgs a) {
         const float inv = 1.f / pa::row_bcast<g>(lt);
         float o[Geo::kCols];
 #pragma unroll
-        for (int c = 0; c < Geo::kCols; ++c) {
-          o[c] = pa::rows_sum(st.o[g][c] * f);
-        }
+        for (int c = 0; c < Geo::kCols; ++c) o[c] = pa::rows_sum(st.o[g][c] * f);
         if (g < G && (g & 3) == jr) {
           if (whole) {
             const int64_t base = (((int64_t)s.b * H_kv + s.kvh) * G + g) * D + c16 * Geo::kCols;
@@ -454,13 +497,13 @@ decode_kernel(DecodeArgs a) {
             for (int c = 0; c < Geo::kCols; ++c) store_out<E>(a.out, base + c, o[c] * inv);
           } else {
 #pragma unroll
-            for (int c = 0; c < Geo::kCols; ++c) slot[g * D + c16 * Geo::kCols + c] = o[c];
+            for (int c = 0; c < Geo::kCols; ++c) P.o[slot][g][c16 * Geo::kCols + c] = o[c];
           }
         }
       });
       if (!whole && lane < G) {
-        a.ws_m[pslot * G + lane] = M;
-        a.ws_l[pslot * G + lane] = lt;
+        P.m[slot][lane] = M;
+        P.l[slot][lane] = lt;
       }
     }
   };
@@ -469,21 +512,19 @@ decode_kernel(DecodeArgs a) {
     State st;
     st.reset();
     if constexpr (!kSmall) {
-      // ---- the share as a stream of batches of up to NBUF tiles.  A batch
-      // holds the remaining tiles of one segment A and, if A ends inside
-      // it, the first tiles of the next segment B, so a share that crosses
-      // a segment boundary costs no extra round trip.  The block ids of the
-      // next batch are fetched (scalar loads; the table is read-only during
-      // the kernel) while the current batch is consumed, and the query rows
+      // ---- the sub-share as a stream of batches of up to NBUF tiles.  A
+      // batch holds the remaining tiles of one segment A and, if A ends
+      // inside it, the first tiles of the next segment B, so a sub-share that
+      // crosses a segment boundary costs no extra round trip.  The query rows
       // of A and B are loaded with the batch's tiles.
       struct Batch {
         Seg A, B;
         int32_t fa;      // flat index of the batch's first tile (in A)
         int32_t nA, n;   // tiles of A; tiles in all (the rest are B's)
-        bool endA, endB; // the segment's last tile in this share is here
+        bool endA, endB; // the segment's last tile in this sub-share is here
       };
-      Seg cs = seg_containing(PB, Ls, B, H_kv, G0);
-      int32_t f = G0;  // next flat tile of the share
+      Seg cs = seg_containing(PB, Ls, B, H_kv, NT, G0);
+      int32_t f = G0;  // next flat tile of the sub-share
       auto next = [&]() {
         Batch bt;
         bt.A = cs;
@@ -496,7 +537,7 @@ decode_kernel(DecodeArgs a) {
         f += bt.nA;
         bt.n = bt.nA;
         if (bt.nA > 0 && f == cs.S1 && f < G1) {
-          seg_advance(cs, PB, Ls, B, H_kv);
+          seg_advance(cs, PB, Ls, B, H_kv, NT);
           if (bt.nA < NBUF && cs.S0 == f) {
             bt.B = cs;
             const int32_t limB = min(cs.S1, G1);
@@ -504,7 +545,7 @@ decode_kernel(DecodeArgs a) {
             bt.endB = f + nB == limB;
             f += nB;
             bt.n += nB;
-            if (f == cs.S1 && f < G1) seg_advance(cs, PB, Ls, B, H_kv);
+            if (f == cs.S1 && f < G1) seg_advance(cs, PB, Ls, B, H_kv, NT);
           }
         }
         if (bt.n == bt.nA) bt.endB = false;
@@ -517,26 +558,27 @@ decode_kernel(DecodeArgs a) {
         kvh = inA ? bt.A.kvh : bt.B.kvh;
         t = bt.fa + uu - (inA ? bt.A.S0 : bt.B.S0);
       };
-      // Block ids of the share, 64 tiles at a time: lane i of chunk c holds
-      // the physical block of flat tile G0 + 64c + i (clamped to the share),
-      // found by a per-lane search of the lengths snapshot and one vector
-      // load from the table, so batches read their block ids from registers
-      // and the table is never on a batch's critical path.
+      // Block ids of the sub-share, 64 tiles at a time: lane i of chunk c
+      // holds the physical block of flat tile G0 + 64c + i (clamped to the
+      // sub-share), found by a per-lane search of the lengths snapshot and one
+      // vector load from the table, so batches read their block ids from
+      // registers and the table is never on a batch's critical path.
       // Indices are clamped into the table so that no snapshot, however
       // inconsistent, can send a read outside it.
       auto chunk_phys = [&](int32_t c) -> int32_t {
         const int32_t fl = min(G0 + 64 * c + lane, G1 - 1);
-        const int32_t b = find_seq(PB, B, H_kv, fl);
-        const int32_t pb = PB[b];
-        const int32_t nt = max(PB[b + 1] - pb, 1);
-        const int32_t r = fl - pb * H_kv;
-        const int32_t t = r - (r / nt) * nt;
+        const int32_t kvh = min(static_cast<int32_t>(static_cast<uint32_t>(fl) /
+                                                     static_cast<uint32_t>(NT)),
+                                H_kv - 1);
+        const int32_t r = fl - kvh * NT;
+        const int32_t b = find_seq(PB, B, r);
+        const int32_t t = r - PB[b];
         const int32_t e = min(max((t * kTile) >> log2_bs, 0), a.max_blocks - 1);
         return a.tables[(int64_t)b * a.max_blocks + e];
       };
       int32_t cbase = G0;  // flat tile of lane 0 of chunk `cur`
       int32_t cur = chunk_phys(0), nxt = 0;
-      if (G1 - G0 > 64) nxt = chunk_phys(1);  // read only by shares of more than 64 tiles
+      if (G1 - G0 > 64) nxt = chunk_phys(1);  // read only by sub-shares of more than 64 tiles
       // Block ids of a batch's tiles, read from the chunks into SGPRs.
       // They are taken for batch k+1 before batch k is consumed, when the
       // chunks are known to have arrived, so that the loop head waits for
@@ -605,9 +647,9 @@ decode_kernel(DecodeArgs a) {
         bt = nx;
       }
     } else {
-      // ---- blocks smaller than a tile: the share as pieces, one per
+      // ---- blocks smaller than a tile: the sub-share as pieces, one per
       // segment, each a pipelined loop over its tiles.
-      Seg s = seg_containing(PB, Ls, B, H_kv, G0);
+      Seg s = seg_containing(PB, Ls, B, H_kv, NT, G0);
       while (true) {
         const int32_t t0 = max(s.S0, G0) - s.S0;
         const int32_t n = min(s.S1, G1) - s.S0 - t0;
@@ -655,146 +697,290 @@ decode_kernel(DecodeArgs a) {
         finish(st, s);
         if (s.S1 >= G1) break;
         st.reset();
-        seg_advance(s, PB, Ls, B, H_kv);
+        seg_advance(s, PB, Ls, B, H_kv, NT);
       }
     }
   }
-}
 
-// Merges the partials of segment blockIdx.x (sequence blockIdx.x / H_kv,
-// KV head blockIdx.x % H_kv) for query head blockIdx.y of the group, if the
-// decode kernel's record says the segment was cut.  The contributors are the
-// waves whose shares meet the segment: consecutive ones from the wave wa
-// holding its first tile when every share is non-empty (T >= W), else one
-// share per tile.  The first contributor's partial is in slot 2w + 1, every
-// later one in slot 2w.  Thread t takes the 4-column group t % (D/4) of the
-// head's row for the contributors congruent to t / (D/4); the slices'
-// (max, sum, output) are then combined through LDS, so the dependent-load
-// depth is n / (number of slices), not n.
-template <int E, int D>
-__global__ void __launch_bounds__(kMergeWG)
-merge_kernel(DecodeArgs a) {
-  constexpr int kCols = D / 4;
-  constexpr int kSlices = kMergeWG / kCols;
-  constexpr int kBatch = 8;  // contributors per thread in flight
-  __shared__ floatx4_t s_acc[kSlices][kCols];
-  __shared__ float s_mx[kSlices], s_den[kSlices];
-  const int32_t* rec = a.records + blockIdx.x * kRecInts;
-  if (rec[0] == 0) return;
-  const int32_t G = a.G, g = blockIdx.y;
-  const int32_t b = blockIdx.x / a.H_kv, kvh = blockIdx.x % a.H_kv;
-  const int32_t S0 = rec[1], S1 = rec[2], Tt = rec[3], W = rec[4], wa = rec[5];
-  // With one tile per non-empty share (T < W <= kMaxWaves), the share of
-  // tile f is ((f + 1) W - 1) / T, small enough for 32-bit arithmetic.
-  const int32_t n = Tt >= W ? share_of(S1 - 1, Tt, W) - wa + 1 : S1 - S0;
-  auto slot_of = [&](int32_t i) {
-    const int32_t w = Tt >= W ? wa + i : ((S0 + i + 1) * W - 1) / Tt;
-    return 2 * w + (i == 0 ? 1 : 0);
-  };
-  const int col = threadIdx.x % kCols, k = threadIdx.x / kCols;
-  float mx = -3.0e38f, den = 0.f;
-  floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int32_t i0 = k; i0 < n; i0 += kSlices * kBatch) {
-    // Unconditional loads (indices past n repeat contributor i0), masked
-    // afterwards, so every load of the batch is in flight at once.
-    float pm[kBatch], pl[kBatch];
-    floatx4_t po[kBatch];
+  // ---- workgroup step: combine the pieces each segment left in LDS.
+  __syncthreads();
+  // Slots in flat order (slot 2v holds the piece at the start of wave v's
+  // sub-share, 2v + 1 the one at its end); the valid slots of one segment
+  // form a run.  The descriptors are read once into registers (every
+  // thread reads the same values, so the control flow below is uniform)
+  // and the slots are walked in one unrolled pass: a piece joins the
+  // running state of its run by the rescaled-sum rule, and at the end of a
+  // run the state is written out (segment inside the share) or published.
+  // At most two runs reach past the share (the one holding its first tile
+  // and the one holding its last); their states are published in piece slot
+  // 2 lw (began before the share) or 2 lw + 1, at device scope.
+  // The eight descriptors are read at once.  Bit k of vmask: slot k holds
+  // a piece; of emask: it ends a run (the next valid slot holds another
+  // segment).  Masks rather than arrays indexed at run time, which would live
+  // in scratch memory.
+  int4 dsc[kSlots];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int32_t i = i0 + u * kSlices;
-      const int32_t slot = slot_of(i < n ? i : i0);
-      pm[u] = a.ws_m[slot * G + g];
-      pl[u] = a.ws_l[slot * G + g];
-      po[u] = *reinterpret_cast<const floatx4_t*>(a.ws_o + ((int64_t)slot * G + g) * D + 4 * col);
+  for (int k = 0; k < kSlots; ++k) dsc[k] = P.seg[k];
+  uint32_t vmask = 0, emask = 0;
+  {
+    int32_t nextS0 = -1;  // S0 of the next valid slot (-1: none)
+#pragma unroll
+    for (int k = kSlots - 1; k >= 0; --k) {
+      if (dsc[k].w) {
+        vmask |= 1u << k;
+        if (nextS0 != dsc[k].x) emask |= 1u << k;
+        nextS0 = dsc[k].x;
+      }
     }
-    float cm = mx;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (i0 + u * kSlices < n) cm = fmaxf(cm, pm[u]);
-    const float r = __builtin_amdgcn_exp2f(mx - cm);
-    acc *= r;
-    den *= r;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const float f = i0 + u * kSlices < n ? __builtin_amdgcn_exp2f(pm[u] - cm) : 0.f;
-      acc += f * po[u];
-      den = fmaf(f, pl[u], den);
-    }
-    mx = cm;
   }
-  s_acc[k][col] = acc;
-  if (col == 0) {
-    s_mx[k] = mx;
-    s_den[k] = den;
+  // The published runs (S0, S1, b | kvh << 16) in scalars, assigned by
+  // selects (a dynamically indexed array, or a reference to either set,
+  // would live in scratch memory).
+  int32_t pub_n = 0;
+  int32_t p0S0 = 0, p0S1 = 0, p0bh = 0, p1S0 = 0, p1S1 = 0, p1bh = 0;
+#pragma unroll
+  for (int k = 0; k < kSlots; ++k) {
+    if ((emask >> k & 1) && !(dsc[k].x >= A0 && dsc[k].y <= A1)) {  // uniform
+      const bool first = pub_n == 0;
+      p0S0 = first ? dsc[k].x : p0S0;
+      p0S1 = first ? dsc[k].y : p0S1;
+      p0bh = first ? dsc[k].z : p0bh;
+      p1S0 = first ? p1S0 : dsc[k].x;
+      p1S1 = first ? p1S1 : dsc[k].y;
+      p1bh = first ? p1bh : dsc[k].z;
+      ++pub_n;
+    }
+  }
+  // Each thread combines one (head, 4-column group) item of every run: the
+  // slots' values are read once, then each run takes the slots of its mask
+  // (selects, not multiplications, keep the garbage of unused slots out).
+  // The code is kept short: at the end of the kernel each SIMD runs one
+  // wave, and every instruction on this path costs its full latency.
+  for (int32_t e = tid; e < G * kC4; e += kWG) {
+    const int32_t g = e / kC4, c4 = e - g * kC4;
+    float sm[kSlots], sl[kSlots];
+    floatx4_t so[kSlots];
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k) {
+      sm[k] = P.m[k][g];
+      sl[k] = P.l[k][g];
+      so[k] = *reinterpret_cast<const floatx4_t*>(&P.o[k][g][4 * c4]);
+    }
+    for (uint32_t rest = vmask; rest != 0;) {  // one run per iteration (uniform)
+      const int k0 = __builtin_ctz(rest);
+      const int k1 = __builtin_ctz(emask & ~((1u << k0) - 1));  // its last slot
+      const uint32_t rm = vmask & ((2u << k1) - 1) & ~((1u << k0) - 1);
+      rest &= ~((2u << k1) - 1);
+      float M = -3.0e38f;
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) M = (rm >> k & 1) ? fmaxf(M, sm[k]) : M;
+      floatx4_t O = {0.f, 0.f, 0.f, 0.f};
+      float Lsum = 0.f;
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) {
+        const bool in = rm >> k & 1;
+        const float w = __builtin_amdgcn_exp2f(sm[k] - M);
+        const floatx4_t x = w * so[k];
+        O[0] += in ? x[0] : 0.f;
+        O[1] += in ? x[1] : 0.f;
+        O[2] += in ? x[2] : 0.f;
+        O[3] += in ? x[3] : 0.f;
+        Lsum += in ? w * sl[k] : 0.f;
+      }
+      const int4 d = P.seg[k1];
+      const int32_t S0 = d.x, S1 = d.y, b = d.z & 0xFFFF, kvh = d.z >> 16;
+      if (S0 >= A0 && S1 <= A1) {
+        store_out4<E>(a.out, (((int64_t)b * H_kv + kvh) * G + g) * D + 4 * c4, O * (1.f / Lsum));
+      } else {
+        // Published written through to memory, so that the merger can read
+        // it from any XCD.
+        const int32_t ps = 2 * lw + (S0 < A0 ? 0 : 1);
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            a.ws_o + (int64_t)ps * G * D, 0, G * D * 4, pa::kRsrcWord3);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, O), ro,
+                                               (g * D + 4 * c4) * 4, 0, kDeviceScope);
+        if (c4 == 0) {
+          const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(
+              a.ws_ml + (int64_t)ps * G * 2, 0, G * 8, pa::kRsrcWord3);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, f32x2_t{M, Lsum}),
+                                                rml, g * 8, 0, kDeviceScope);
+        }
+      }
+    }
+  }
+  pub_n = min(pub_n, 2);
+  if (pub_n == 0) return;  // uniform
+
+  // ---- publish: the pieces are complete at device scope before the
+  // arrival is counted.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // Contributors of published run j: the logical workgroups la.. whose
+  // shares meet the segment, n of them.
+  auto first_of = [&](int32_t S0) { return share_of(S0, Tt, nwg); };
+  auto count_of = [&](int32_t S0, int32_t S1) {
+    return Tt >= nwg ? share_of(S1 - 1, Tt, nwg) - share_of(S0, Tt, nwg) + 1 : S1 - S0;
+  };
+  if (tid < pub_n) {
+    const int32_t S0 = tid == 0 ? p0S0 : p1S0, S1 = tid == 0 ? p0S1 : p1S1;
+    const int32_t bh = tid == 0 ? p0bh : p1bh, b = bh & 0xFFFF, kvh = bh >> 16;
+    const int32_t n = count_of(S0, S1);
+    // Arrival: the count in bits 0-15, the sum of the contributors' XCD
+    // numbers x in bits 16-31 and of x^2 in bits 32-47 (n <= 1024, x <= 7).
+    // The n contributors ran on one XCD iff n * sum(x^2) = sum(x)^2, and on
+    // this one iff moreover sum(x) = n * x.
+    const uint64_t x = static_cast<uint64_t>(xcd_id());
+    const uint64_t inc = 1 + (x << 16) + ((x * x) << 32);
+    uint64_t* ctr = a.counters + (int64_t)kvh * B + b;
+    const uint64_t tot = __hip_atomic_fetch_add(ctr, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+    const uint64_t cnt = tot & 0xFFFF, s1 = (tot >> 16) & 0xFFFF, s2 = (tot >> 32) & 0xFFFF;
+    const bool last = cnt == static_cast<uint64_t>(n);
+    if (last) __hip_atomic_store(ctr, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool here = cnt * s2 == s1 * s1 && s1 == cnt * x;
+    P.flag[tid] = last ? (here ? 1 : 2) : 0;
   }
   __syncthreads();
-  if (k != 0) return;
-  float M = s_mx[0];
+
+  // ---- the last contributor merges: out = sum_i 2^(m_i - M) o_i /
+  // sum_i 2^(m_i - M) l_i over the pieces in flat order (so the result does
+  // not depend on which workgroup arrived last), rounded once.  Pieces that
+  // all went through this XCD's L2 are read from there; otherwise at device
+  // scope.  Both published runs (if this workgroup is last for both) are
+  // merged together, so their loads are in flight at once.  The kC4 lanes
+  // that share a head each fetch one contributor's (max, sum) and pass them
+  // round by shuffles, so a lane issues one 8-byte load per kC4
+  // contributors besides its 16-byte output loads.
+  const int32_t f0 = P.flag[0], f1 = pub_n > 1 ? P.flag[1] : 0;
+  const int nm = (f0 ? 1 : 0) + (f1 ? 1 : 0);
+  if (nm == 0) return;  // uniform
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(a.ws_o, 0, 0x7FFFFFFF, pa::kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(a.ws_ml, 0, 0x7FFFFFFF, pa::kRsrcWord3);
+  const int32_t sub = lane & (kC4 - 1), base = lane - sub;  // lane within its head's group
+  for (int32_t e0 = 0; e0 < nm * G * kC4; e0 += kWG) {  // uniform
+    const int32_t e = min(e0 + tid, nm * G * kC4 - 1);  // spare lanes repeat the last item
+    const bool live = e0 + tid < nm * G * kC4;
+    const int j = (e >= G * kC4 || !f0) ? 1 : 0;  // published run of this item
+    const int32_t ej = e - (e >= G * kC4 ? G * kC4 : 0);
+    const int32_t g = ej / kC4, c4 = ej - g * kC4;
+    const int32_t S0 = j ? p1S0 : p0S0, S1 = j ? p1S1 : p0S1;
+    const int32_t bh = j ? p1bh : p0bh, b = bh & 0xFFFF, kvh = bh >> 16;
+    const bool device_scope = (j ? f1 : f0) == 2;
+    const int32_t la = share_of(S0, Tt, nwg), n = count_of(S0, S1);
+    // Piece slot of contributor i: the first holds the segment's start
+    // (slot 1 of its workgroup), every later one began before its share.
+    auto piece = [&](int32_t i) {
+      const int32_t l = Tt >= nwg ? la + i : share_of(S0 + i, Tt, nwg);
+      return 2 * l + (i == 0 ? 1 : 0);
+    };
+    // n is uniform within each group of kC4 lanes (one item of one run), so
+    // the loops below are too; the shuffles stay inside the group.  Each
+    // lane finds one contributor's piece slot and (max, sum); the slots of
+    // the others come by shuffle, so the output loads of a batch need no
+    // index arithmetic between them.
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (!device_scope) {
+      float mx = -3.0e38f;
+      for (int32_t i0 = 0; i0 < n; i0 += kC4) {
+        const int32_t cn = min(kC4, n - i0);
+        const int32_t mine = piece(i0 + min(sub, cn - 1));
+        const f32x2_t ml = __builtin_bit_cast(
+            f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, (mine * G + g) * 8, 0, 0));
+        constexpr int kBatch = 16;  // output loads in flight per lane
+        for (int32_t u0 = 0; u0 < cn; u0 += kBatch) {
+          floatx4_t po[kBatch];
 #pragma unroll
-  for (int j = 1; j < kSlices; ++j) M = fmaxf(M, s_mx[j]);
-  floatx4_t o = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
+          for (int u = 0; u < kBatch; ++u) {
+            // Unconditional loads (indices past cn repeat the chunk's last),
+            // masked afterwards, so every load of the batch is in flight.
+            const int32_t ps = __shfl(mine, base + min(u0 + u, cn - 1));
+            po[u] = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      ro, ((ps * G + g) * D + 4 * c4) * 4, 0, 0));
+          }
+          // The (max, sum) shuffles wait for their load; keep them after the
+          // output loads so that one round trip covers both.
+          __builtin_amdgcn_sched_barrier(0);
+          float pm[kBatch], pl[kBatch];
 #pragma unroll
-  for (int j = 0; j < kSlices; ++j) {
-    const float f = __builtin_amdgcn_exp2f(s_mx[j] - M);  // 0 for an empty slice
-    o += f * s_acc[j][col];
-    l = fmaf(f, s_den[j], l);
-  }
-  const float inv = 1.f / l;
-  const int64_t base = (((int64_t)b * a.H_kv + kvh) * G + g) * D + 4 * col;
-  if constexpr (E != 0) {
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + base) =
-        uint2{pa::pack2<E>(o[0] * inv, o[1] * inv), pa::pack2<E>(o[2] * inv, o[3] * inv)};
-  } else {
-    *reinterpret_cast<floatx4_t*>(reinterpret_cast<float*>(a.out) + base) = o * inv;
+          for (int u = 0; u < kBatch; ++u) {
+            const int src = base + min(u0 + u, cn - 1);
+            pm[u] = __shfl(ml[0], src);
+            pl[u] = __shfl(ml[1], src);
+          }
+          float cm = mx;
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (u0 + u < cn) cm = fmaxf(cm, pm[u]);
+          const float r = __builtin_amdgcn_exp2f(mx - cm);
+          acc *= r;
+          den *= r;
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const float w = u0 + u < cn ? __builtin_amdgcn_exp2f(pm[u] - cm) : 0.f;
+            acc += w * po[u];
+            den = fmaf(w, pl[u], den);
+          }
+          mx = cm;
+        }
+      }
+    } else {
+      // Some contributor ran on another XCD than this one: read every
+      // piece at device scope, one at a time (a rare path, kept short).
+      float mx = -3.0e38f;
+      for (int32_t i = 0; i < n; ++i) {
+        const int32_t ps = piece(i);
+        const f32x2_t ml = __builtin_bit_cast(
+            f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, (ps * G + g) * 8, 0, kDeviceScope));
+        const floatx4_t o = __builtin_bit_cast(floatx4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              ro, ((ps * G + g) * D + 4 * c4) * 4, 0,
+                                                              kDeviceScope));
+        const float cm = fmaxf(mx, ml[0]);
+        const float r = __builtin_amdgcn_exp2f(mx - cm), w = __builtin_amdgcn_exp2f(ml[0] - cm);
+        acc = acc * r + w * o;
+        den = den * r + w * ml[1];
+        mx = cm;
+      }
+    }
+    if (live)
+      store_out4<E>(a.out, (((int64_t)b * H_kv + kvh) * G + g) * D + 4 * c4, acc * (1.f / den));
   }
 }
 
 // ----------------------------------------------------------- host helpers
-int decode_wgs(int nw) {
-  // Tuning override (read on every call): PA_DECODE_WGS = workgroups of
-  // the decode grid.  Any value gives the same result up to fp32 rounding.
-  const char* e = std::getenv("PA_DECODE_WGS");
-  const int x = e ? std::atoi(e) : kDefaultWGs;
-  return x >= 1 && x * nw <= kMaxWaves ? x : kDefaultWGs;
-}
-
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t rec_off, o_off, m_off, l_off, total;
+  size_t ctr_off, o_off, ml_off, total;
 };
 
+// Counters first (the part that must be zero), then the published pieces.
 WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t H_q, int32_t B) {
   const size_t G = H_q / d->num_kv_heads;
+  const size_t slots = 2 * (size_t)kMaxWGs;
   WorkspaceLayout w;
-  w.rec_off = 0;
-  w.o_off = align_up((size_t)B * d->num_kv_heads * kRecInts * sizeof(int32_t), 256);
-  w.m_off = w.o_off + align_up((size_t)2 * kMaxWaves * G * d->head_dim * sizeof(float), 256);
-  w.l_off = w.m_off + align_up((size_t)2 * kMaxWaves * G * sizeof(float), 256);
-  w.total = w.l_off + align_up((size_t)2 * kMaxWaves * G * sizeof(float), 256);
+  w.ctr_off = 0;
+  w.o_off = align_up((size_t)B * d->num_kv_heads * sizeof(uint64_t), 256);
+  w.ml_off = w.o_off + align_up(slots * G * d->head_dim * sizeof(float), 256);
+  w.total = w.ml_off + align_up(slots * G * 2 * sizeof(float), 256);
   return w;
 }
 
-// Waves per workgroup and tiles per batch.  Waves are independent, so the
-// workgroup size only sets how often the lengths prologue is repeated.
+// Tiles per batch.  fp32 pools with large query groups hold G*D/16 output
+// floats per lane in registers, which leaves room for one tile per batch.
 template <bool k16, int D, int GP>
-struct Config {
-  static constexpr int kNW = PA_DECODE_NW;
-  // fp32 pools with large query groups hold G*D/16 output floats per lane
-  // in registers, which leaves room for one tile per batch only.
-  static constexpr int NBUF =
-      k16 ? (GP >= 8 ? 2 : PA_DECODE_NB_BF16) : (GP * D >= 8 * 64 ? 1 : 2);
-};
+constexpr int kNbuf = k16 ? (GP >= 8 ? 2 : PA_DECODE_NB_BF16) : (GP * D >= 8 * 64 ? 1 : 2);
 
-size_t lds_bytes(int nw, int32_t B) { return (size_t)(2 * B + 1 + nw) * sizeof(int32_t); }
+template <int D, int GP>
+size_t lds_bytes(int32_t B) {
+  return sizeof(LdsPieces<D, GP>) + (size_t)(2 * B + 1 + kNW) * sizeof(int32_t);
+}
 
 template <int E, int D, int GP>
-pa_status launch(const DecodeArgs& a, hipStream_t s) {
-  using C = Config<(E != 0), D, GP>;
-  auto kern = a.log2_bs >= 4 ? decode_kernel<E, D, GP, C::kNW, C::NBUF, false>
-                             : decode_kernel<E, D, GP, C::kNW, C::NBUF, true>;
-  const size_t lds = lds_bytes(C::kNW, a.B);
+pa_status launch(const DecodeArgs& a, int wgs, hipStream_t s) {
+  constexpr int NBUF = kNbuf<(E != 0), D, GP>;
+  auto kern = a.log2_bs >= 4 ? decode_kernel<E, D, GP, NBUF, false>
+                             : decode_kernel<E, D, GP, NBUF, true>;
+  const size_t lds = lds_bytes<D, GP>(a.B);
   if (lds > kMaxLds)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: %d sequences need %zu bytes of LDS (> %zu)",
                     a.B, lds, kMaxLds);
@@ -804,21 +990,19 @@ pa_status launch(const DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess)
       return pa::fail(PA_ERR_DEVICE, "pa_decode: LDS attribute: %s", hipGetErrorString(e));
   }
-  const int wgs = decode_wgs(C::kNW);
-  hipLaunchKernelGGL(kern, dim3(wgs), dim3(C::kNW * kWave), lds, s, a);
-  hipLaunchKernelGGL((merge_kernel<E, D>), dim3(a.B * a.H_kv, a.G), dim3(kMergeWG), 0, s, a);
+  hipLaunchKernelGGL(kern, dim3(wgs), dim3(kWG), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return pa::fail(PA_ERR_DEVICE, "pa_decode: %s", hipGetErrorString(e));
   return PA_OK;
 }
 
 template <int E, int D>
-pa_status dispatch_g(const DecodeArgs& a, hipStream_t s) {
-  if (a.G <= 1) return launch<E, D, 1>(a, s);
-  if (a.G <= 2) return launch<E, D, 2>(a, s);
-  if (a.G <= 4) return launch<E, D, 4>(a, s);
-  if (a.G <= 8) return launch<E, D, 8>(a, s);
-  return launch<E, D, 16>(a, s);
+pa_status dispatch_g(const DecodeArgs& a, int wgs, hipStream_t s) {
+  if (a.G <= 1) return launch<E, D, 1>(a, wgs, s);
+  if (a.G <= 2) return launch<E, D, 2>(a, wgs, s);
+  if (a.G <= 4) return launch<E, D, 4>(a, wgs, s);
+  if (a.G <= 8) return launch<E, D, 8>(a, wgs, s);
+  return launch<E, D, 16>(a, wgs, s);
 }
 
 }  // namespace
@@ -866,13 +1050,12 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     max_blocks_per_seq);
   if (num_seqs > kMaxSeqs)
     return pa::fail(PA_ERR_UNSUPPORTED, "num_seqs %d > %d", num_seqs, kMaxSeqs);
+  if (desc->num_kv_heads > kMaxKvHeads)
+    return pa::fail(PA_ERR_UNSUPPORTED, "num_kv_heads %d > %d", desc->num_kv_heads, kMaxKvHeads);
   const int64_t len_cap = (int64_t)max_blocks_per_seq * block_size;
   if (len_cap > INT32_MAX)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "max_blocks_per_seq * block_size overflows int32");
-  // Segment records and flat tile indices (sequence, KV head, tile) must fit
-  // in int32.
-  if ((int64_t)num_seqs * desc->num_kv_heads * kRecInts >= (1ll << 31))
-    return pa::fail(PA_ERR_UNSUPPORTED, "num_seqs * KV heads too large");
+  // Flat tile indices (KV head, sequence, tile) must fit in int32.
   if ((int64_t)num_seqs * ((len_cap + kTile - 1) / kTile) * desc->num_kv_heads >= (1ll << 31))
     return pa::fail(PA_ERR_UNSUPPORTED, "num_seqs * tiles per sequence * KV heads >= 2^31");
   if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
@@ -888,6 +1071,8 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (workspace_bytes < wl.total)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace %zu bytes < %zu needed", workspace_bytes,
                     wl.total);
+  const int32_t tuned = pa::tuning(PA_TUNE_DECODE_WORKGROUPS);
+  const int wgs = tuned >= 1 && tuned <= kMaxWGs ? tuned : kDefaultWGs;
   char* ws = reinterpret_cast<char*>(workspace);
   DecodeArgs a;
   a.q = q;
@@ -896,10 +1081,9 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   a.tables = block_tables;
   a.lens = context_lens;
   a.out = out;
-  a.records = reinterpret_cast<int32_t*>(ws + wl.rec_off);
+  a.counters = reinterpret_cast<uint64_t*>(ws + wl.ctr_off);
   a.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
-  a.ws_m = reinterpret_cast<float*>(ws + wl.m_off);
-  a.ws_l = reinterpret_cast<float*>(ws + wl.l_off);
+  a.ws_ml = reinterpret_cast<float*>(ws + wl.ml_off);
   a.B = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = desc->num_blocks;
@@ -910,9 +1094,9 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   hipStream_t s = (hipStream_t)stream;
   const bool d128 = desc->head_dim == 128;
   switch (desc->dtype) {
-    case PA_BF16: return d128 ? dispatch_g<1, 128>(a, s) : dispatch_g<1, 64>(a, s);
-    case PA_F16: return d128 ? dispatch_g<2, 128>(a, s) : dispatch_g<2, 64>(a, s);
-    default: return d128 ? dispatch_g<0, 128>(a, s) : dispatch_g<0, 64>(a, s);
+    case PA_BF16: return d128 ? dispatch_g<1, 128>(a, wgs, s) : dispatch_g<1, 64>(a, wgs, s);
+    case PA_F16: return d128 ? dispatch_g<2, 128>(a, wgs, s) : dispatch_g<2, 64>(a, wgs, s);
+    default: return d128 ? dispatch_g<0, 128>(a, wgs, s) : dispatch_g<0, 64>(a, wgs, s);
   }
 }
 

@@ -18,6 +18,10 @@ inline int elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
 // Validates a pool descriptor against the supported set (see pa.h).
 pa_status check_desc(const pa_cache_desc* desc);
 
+// Current value of a process-wide tuning knob (0 = automatic); see
+// pa_set_tuning.
+int32_t tuning(pa_tuning_key key);
+
 // True if p is a multiple of `bytes` (a power of two).
 inline bool aligned(const void* p, uintptr_t bytes) {
   return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;

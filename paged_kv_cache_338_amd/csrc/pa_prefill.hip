@@ -741,8 +741,8 @@ inline size_t align_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 // long.  Measured on the worked batch (last N tokens of each sequence): N =
 // 64 took 51 us split against 91 us whole, N = 128 68 against 94 (pieces of
 // 48 tiles; 4-16 tile pieces were up to 4x slower), while N = 256 (928
-// items) took 100 us whole and 109-115 us split.  Tuning override (read on
-// every call): PA_PREFILL_KEY_TILES.
+// items) took 100 us whole and 109-115 us split.  The piece length can be
+// set with pa_set_tuning(PA_TUNE_PREFILL_KEY_TILES, n).
 struct SplitPlan {
   bool split;
   int32_t key_tiles;
@@ -762,10 +762,7 @@ SplitPlan split_plan(const pa_cache_desc* d, int32_t B, int32_t H_q, int32_t T, 
   if (items1 > kSplitMaxItems || prefill_items(T, B, H_kv, GP, 2) >= kMinItemsR2) return p;
   const int64_t maxtiles = ((int64_t)maxb * d->block_size + kKT - 1) / kKT;
   int64_t kt = std::max<int64_t>(kMinKeyTiles, (maxtiles * items1 + kSplitGrid - 1) / kSplitGrid);
-  if (const char* e = std::getenv("PA_PREFILL_KEY_TILES")) {
-    const int x = std::atoi(e);
-    if (x >= 1) kt = x;
-  }
+  if (const int32_t x = pa::tuning(PA_TUNE_PREFILL_KEY_TILES); x >= 1) kt = x;
   const int64_t S = (maxtiles + kt - 1) / kt;
   if (S <= 1 || items1 * S >= (1ll << 31)) return p;
   p.split = true;

@@ -1,5 +1,6 @@
 // Status names, the thread-local last-error text and the shape checks of
 // the C ABI (host code).
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -8,6 +9,8 @@
 
 namespace {
 thread_local std::string g_last_error;
+// Tuning knobs, indexed by pa_tuning_key; 0 = the library's own choice.
+std::atomic<int32_t> g_tuning[3];
 }
 
 namespace pa {
@@ -27,6 +30,10 @@ int ilog2_exact(int32_t x) {
   int l = 0;
   while ((1 << l) < x) ++l;
   return l;
+}
+
+int32_t tuning(pa_tuning_key key) {
+  return key >= 1 && key <= 2 ? g_tuning[key].load(std::memory_order_relaxed) : 0;
 }
 
 pa_status check_desc(const pa_cache_desc* desc) {
@@ -50,6 +57,31 @@ pa_status check_desc(const pa_cache_desc* desc) {
 extern "C" {
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+pa_status pa_set_tuning(pa_tuning_key key, int32_t value) {
+  switch (key) {
+    case PA_TUNE_DECODE_WORKGROUPS:
+      if (value < 0 || value > 1024)
+        return pa::fail(PA_ERR_INVALID_ARGUMENT, "decode workgroups %d not in [0, 1024]", value);
+      break;
+    case PA_TUNE_PREFILL_KEY_TILES:
+      if (value < 0 || value > (1 << 20))
+        return pa::fail(PA_ERR_INVALID_ARGUMENT, "prefill key tiles %d not in [0, 2^20]", value);
+      break;
+    default:
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "unknown tuning key %d", key);
+  }
+  g_tuning[key].store(value, std::memory_order_relaxed);
+  return PA_OK;
+}
+
+pa_status pa_get_tuning(pa_tuning_key key, int32_t* value) {
+  if (!value) return pa::fail(PA_ERR_INVALID_ARGUMENT, "value is NULL");
+  if (key != PA_TUNE_DECODE_WORKGROUPS && key != PA_TUNE_PREFILL_KEY_TILES)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "unknown tuning key %d", key);
+  *value = pa::tuning(key);
+  return PA_OK;
+}
 
 const char* pa_status_string(pa_status status) {
   switch (status) {

@@ -289,16 +289,21 @@ def test_physical_relabelling_is_bit_identical():
     assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
-@pytest.mark.parametrize("wgs", ["1", "3", "97", "256", "1024"])
-def test_grid_size_does_not_change_the_result(wgs, monkeypatch):
+@pytest.mark.parametrize("wgs", [1, 3, 8, 97, 256, 264, 1024])
+def test_grid_size_does_not_change_the_result(wgs):
     # The grid splits the flat tile list into equal shares; a share boundary
-    # inside a (sequence, KV head) segment leaves partials that the last
-    # workgroup to arrive merges.  Any grid size must give the same result.
+    # inside a (KV head, sequence) segment leaves partials that the last
+    # workgroup to arrive merges, from its own L2 when every piece ran on
+    # one XCD, else at device scope (grids that are not a multiple of 8 deal
+    # consecutive shares to different XCDs).  Any grid size must give the
+    # same result.
+    import paged_kv_cache_338_amd as pa
     w = W.llama3_8b_decode()
     oc, gc = run_both(w)
     want = oc.decode()
-    monkeypatch.setenv("PA_DECODE_WGS", wgs)
-    assert_close(w, gc.decode(), want)
+    with pa.tuning(pa.PA_TUNE_DECODE_WORKGROUPS, wgs):
+        got = gc.decode()
+    assert_close(w, got, want)
 
 
 def test_copy_blocks_direct_bit_exact():
@@ -349,10 +354,12 @@ def test_python_binding_rejects_bad_arguments():
         pa.pa_decode(q, kc, kc, t.long(), l, 16, 1.0, torch.empty_like(q))
 
 
-def test_workspace_needs_no_initialisation_and_is_reusable(monkeypatch):
-    # Every call writes each workspace record and partial before reading it,
-    # so a garbage-filled workspace works and one workspace serves any number
-    # of calls and grid sizes.
+def test_workspace_zero_filled_once_serves_every_call():
+    # Only the arrival counters must start at zero (they are the first
+    # B * H_kv 64-bit words of the workspace, padded to 256 bytes); every call puts
+    # them back to zero, and writes each published piece before it is read,
+    # so garbage elsewhere is harmless and one workspace serves any number of
+    # calls and grid sizes, with the counters zero after each.
     import torch
     import paged_kv_cache_338_amd as pa
     w = W.llama3_8b_decode()
@@ -363,13 +370,17 @@ def test_workspace_needs_no_initialisation_and_is_reusable(monkeypatch):
     td = torch.from_numpy(tables).to(gc.device)
     ld = torch.from_numpy(lens).to(gc.device)
     ws = pa.decode_workspace(gc.k_cache, w.batch, w.num_q_heads, tables.shape[1])
+    nctr = -(-w.batch * w.num_kv_heads * 8 // 256) * 256
     ws.fill_(0xFF)
-    for wgs in ("256", "1000", "37", "256", "1"):
-        monkeypatch.setenv("PA_DECODE_WGS", wgs)
-        out = torch.empty_like(qd)
-        pa.pa_decode(qd, gc.k_cache, gc.v_cache, td, ld, w.block_size, w.scale, out, workspace=ws)
+    ws[:nctr].zero_()
+    for wgs in (256, 1000, 37, 256, 1, 512):
+        with pa.tuning(pa.PA_TUNE_DECODE_WORKGROUPS, wgs):
+            out = torch.empty_like(qd)
+            pa.pa_decode(qd, gc.k_cache, gc.v_cache, td, ld, w.block_size, w.scale, out,
+                         workspace=ws)
         torch.cuda.synchronize()
         assert_close(w, out, want)
+        assert not ws[:nctr].any(), wgs
 
 
 def test_graph_replay_matches_eager_and_reads_lengths_at_run_time():

@@ -25,6 +25,16 @@ def gpu():
     yield
 
 
+@pytest.fixture
+def key_tiles_knob():
+    """Sets the split prefill's piece length (key tiles) for one test and
+    restores it afterwards."""
+    import paged_kv_cache_338_amd as pa
+    old = pa.pa_get_tuning(pa.PA_TUNE_PREFILL_KEY_TILES)
+    yield lambda n: pa.pa_set_tuning(pa.PA_TUNE_PREFILL_KEY_TILES, int(n))
+    pa.pa_set_tuning(pa.PA_TUNE_PREFILL_KEY_TILES, old)
+
+
 def _bits(x, dtype):
     return W.round_to_bf16_bits(x) if dtype == "bf16" else W.round_to_f16_bits(x)
 
@@ -292,12 +302,12 @@ def _check_split(seed, lengths, nq, dtype="bf16", **kw):
 
 @pytest.mark.parametrize("key_tiles", ["1", "3"])
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"G{s[0]}_H{s[1]}_D{s[2]}_bs{s[3]}" for s in SHAPES])
-def test_split_shapes(shape, key_tiles, monkeypatch):
+def test_split_shapes(shape, key_tiles, key_tiles_knob):
     """Every shape of the unsplit test with the key range cut into pieces of
     1 or 3 key tiles (32 or 96 keys): pieces whose keys a row does not see
     (before its causal limit) must drop out of the merge, and the last piece
     of a block is short."""
-    monkeypatch.setenv("PA_PREFILL_KEY_TILES", key_tiles)
+    key_tiles_knob(key_tiles)
     G, H_kv, D, bs, lengths, nq = shape
     _check_split(sum(lengths) + G + 7, lengths, nq, G=G, H_kv=H_kv, D=D, bs=bs)
 
@@ -318,11 +328,11 @@ def test_split_llama_shape_chunk64():
     assert float(np.abs(got - whole).max()) <= TOL["bf16"]
 
 
-def test_split_rising_logits(monkeypatch):
+def test_split_rising_logits(key_tiles_knob):
     """Logits rising along the keys: every later piece has a larger reference
     maximum than the earlier ones, so the merge must rescale each piece by
     2^(m_i - M) (pieces of 2 key tiles)."""
-    monkeypatch.setenv("PA_PREFILL_KEY_TILES", "2")
+    key_tiles_knob("2")
     lengths, nq = [700, 333], [30, 33]
     q, k, v, t, lens, qs, bs = _case(78, lengths, nq, G=4, H_kv=2, D=128)
     q[:] = W.round_to_bf16_bits(np.full(q.shape, 0.125, np.float32))
@@ -335,8 +345,8 @@ def test_split_rising_logits(monkeypatch):
     assert float(np.abs(got - want).max()) <= TOL["bf16"]
 
 
-def test_split_f16_and_negative_scale(monkeypatch):
-    monkeypatch.setenv("PA_PREFILL_KEY_TILES", "2")
+def test_split_f16_and_negative_scale(key_tiles_knob):
+    key_tiles_knob("2")
     q, k, v, t, lens, qs, bs = _case(79, [300, 90, 5], [40, 90, 5], G=8, H_kv=1, D=64, bs=8,
                                      dtype="f16")
     for scale in (1.0 / 8, -1.0 / 8):
