@@ -184,7 +184,9 @@ pa_status pa_swap_blocks(const int32_t* src_dst_pairs, int32_t num_pairs, const 
  *               instance by hipMemset or torch.zeros); every call leaves it
  *               ready for the next one (its arrival counters back at zero),
  *               so one zero fill serves any number of calls, graph replays
- *               included.  The call owns it until the stream reaches the end
+ *               included, and a workspace sized for num_seqs = B serves
+ *               every call of the same head shape with num_seqs <= B.
+ *               The call owns it until the stream reaches the end
  *               of the call; calls that share a workspace must be ordered
  *               (one stream, or events): overlapping calls race.
  * num_seqs:     at most 8192 (PA_ERR_UNSUPPORTED beyond, or when the lengths

@@ -950,18 +950,23 @@ decode_kernel(DecodeArgs a) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WorkspaceLayout {
-  size_t ctr_off, o_off, ml_off, total;
+  size_t o_off, ml_off, pieces_end, ctr_off, total;
 };
 
-// Counters first (the part that must be zero), then the published pieces.
+// The published pieces first (their size depends on the head shape only),
+// then the arrival counters (the part that must be zero, one per (KV head,
+// sequence)).  Calls of one head shape with fewer sequences use a prefix of
+// the counters, so a workspace serves every batch size up to the one it was
+// sized for without a new zero fill.
 WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t H_q, int32_t B) {
   const size_t G = H_q / d->num_kv_heads;
   const size_t slots = 2 * (size_t)kMaxWGs;
   WorkspaceLayout w;
-  w.ctr_off = 0;
-  w.o_off = align_up((size_t)B * d->num_kv_heads * sizeof(uint64_t), 256);
-  w.ml_off = w.o_off + align_up(slots * G * d->head_dim * sizeof(float), 256);
-  w.total = w.ml_off + align_up(slots * G * 2 * sizeof(float), 256);
+  w.o_off = 0;
+  w.ml_off = align_up(slots * G * d->head_dim * sizeof(float), 256);
+  w.pieces_end = w.ml_off + align_up(slots * G * 2 * sizeof(float), 256);
+  w.ctr_off = w.pieces_end;
+  w.total = w.ctr_off + align_up((size_t)B * d->num_kv_heads * sizeof(uint64_t), 256);
   return w;
 }
 
@@ -1035,11 +1040,17 @@ pa_status pa_decode_workspace_size(const pa_cache_desc* desc, int32_t num_seqs,
   return PA_OK;
 }
 
-pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
-                    float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks the arguments (all but the workspace) and launches the decode
+// with the given workspace parts.
+pa_status decode_launch(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                        float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
+                        float* ws_o, float* ws_ml, uint64_t* counters, void* stream) {
   pa_status st = pa_supported(desc, num_q_heads);
   if (st != PA_OK) return st;
   if (block_size != desc->block_size)
@@ -1060,20 +1071,14 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     return pa::fail(PA_ERR_UNSUPPORTED, "num_seqs * tiles per sequence * KV heads >= 2^31");
   if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID_ARGUMENT, "scale is not finite");
   if (num_seqs == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !workspace)
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out || !ws_o || !ws_ml ||
+      !counters)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");
-  if (!pa::aligned(workspace, 256))
-    return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
   if (!pa::aligned(q, 16) || !pa::aligned(k_cache, 16) || !pa::aligned(v_cache, 16) ||
       !pa::aligned(out, 16) || !pa::aligned(block_tables, 4) || !pa::aligned(context_lens, 4))
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "misaligned pointer");
-  const WorkspaceLayout wl = workspace_layout(desc, num_q_heads, num_seqs);
-  if (workspace_bytes < wl.total)
-    return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace %zu bytes < %zu needed", workspace_bytes,
-                    wl.total);
   const int32_t tuned = pa::tuning(PA_TUNE_DECODE_WORKGROUPS);
   const int wgs = tuned >= 1 && tuned <= kMaxWGs ? tuned : kDefaultWGs;
-  char* ws = reinterpret_cast<char*>(workspace);
   DecodeArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -1081,9 +1086,9 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   a.tables = block_tables;
   a.lens = context_lens;
   a.out = out;
-  a.counters = reinterpret_cast<uint64_t*>(ws + wl.ctr_off);
-  a.ws_o = reinterpret_cast<float*>(ws + wl.o_off);
-  a.ws_ml = reinterpret_cast<float*>(ws + wl.ml_off);
+  a.counters = counters;
+  a.ws_o = ws_o;
+  a.ws_ml = ws_ml;
   a.B = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = desc->num_blocks;
@@ -1098,6 +1103,36 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     case PA_F16: return d128 ? dispatch_g<2, 128>(a, wgs, s) : dispatch_g<2, 64>(a, wgs, s);
     default: return d128 ? dispatch_g<0, 128>(a, wgs, s) : dispatch_g<0, 64>(a, wgs, s);
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                    float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = pa_supported(desc, num_q_heads);
+  if (st != PA_OK) return st;
+  // The workspace is checked here; every other argument (and a NULL
+  // workspace, as a NULL pointer) by decode_launch, in the header's order.
+  char* ws = reinterpret_cast<char*>(workspace);
+  WorkspaceLayout wl{};
+  if (num_seqs > 0 && num_seqs <= kMaxSeqs && ws) {
+    if (!pa::aligned(workspace, 256))
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    wl = workspace_layout(desc, num_q_heads, num_seqs);
+    if (workspace_bytes < wl.total)
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace %zu bytes < %zu needed",
+                      workspace_bytes, wl.total);
+  }
+  return decode_launch(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, block_size, scale, out, num_q_heads, desc,
+                       ws ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr,
+                       ws ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr,
+                       ws ? reinterpret_cast<uint64_t*>(ws + wl.ctr_off) : nullptr, stream);
 }
 
 }  // extern "C"

@@ -355,10 +355,10 @@ def test_python_binding_rejects_bad_arguments():
 
 
 def test_workspace_zero_filled_once_serves_every_call():
-    # Only the arrival counters must start at zero (they are the first
-    # B * H_kv 64-bit words of the workspace, padded to 256 bytes); every call puts
-    # them back to zero, and writes each published piece before it is read,
-    # so garbage elsewhere is harmless and one workspace serves any number of
+    # Only the arrival counters must start at zero (they follow the
+    # published partial results, B * H_kv 64-bit words); every call puts them
+    # back to zero and writes each published piece before it is read, so
+    # garbage elsewhere is harmless and one workspace serves any number of
     # calls and grid sizes, with the counters zero after each.
     import torch
     import paged_kv_cache_338_amd as pa
@@ -372,7 +372,7 @@ def test_workspace_zero_filled_once_serves_every_call():
     ws = pa.decode_workspace(gc.k_cache, w.batch, w.num_q_heads, tables.shape[1])
     nctr = -(-w.batch * w.num_kv_heads * 8 // 256) * 256
     ws.fill_(0xFF)
-    ws[:nctr].zero_()
+    ws[-nctr:].zero_()
     for wgs in (256, 1000, 37, 256, 1, 512):
         with pa.tuning(pa.PA_TUNE_DECODE_WORKGROUPS, wgs):
             out = torch.empty_like(qd)
@@ -380,7 +380,31 @@ def test_workspace_zero_filled_once_serves_every_call():
                          workspace=ws)
         torch.cuda.synchronize()
         assert_close(w, out, want)
-        assert not ws[:nctr].any(), wgs
+        assert not ws[-nctr:].any(), wgs
+
+
+def test_workspace_serves_smaller_batches_between_larger_ones():
+    # One zero fill serves calls of any batch size up to the one the
+    # workspace was sized for: a call with fewer sequences uses a prefix of
+    # the counters and leaves it at zero, and the published pieces never
+    # overlap the counters (regression: the counters used to come first, so
+    # a larger batch found the pieces of a smaller one there).
+    import torch
+    import paged_kv_cache_338_amd as pa
+    w = W.llama3_8b_decode()
+    oc, gc = run_both(w)
+    want = oc.decode()
+    tables, lens = gc.tables()
+    qd = _gd().to_torch(w.q, w.dtype, gc.device)
+    td = torch.from_numpy(tables).to(gc.device)
+    ld = torch.from_numpy(lens).to(gc.device)
+    ws = pa.decode_workspace(gc.k_cache, w.batch, w.num_q_heads, tables.shape[1])
+    for sl in (slice(0, 8), slice(2, 5), slice(0, 8), slice(6, 8), slice(0, 1), slice(0, 8)):
+        q, t, l = qd[sl].contiguous(), td[sl].contiguous(), ld[sl].contiguous()
+        out = torch.empty_like(q)
+        pa.pa_decode(q, gc.k_cache, gc.v_cache, t, l, w.block_size, w.scale, out, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(w, out, want[sl])
 
 
 def test_graph_replay_matches_eager_and_reads_lengths_at_run_time():
