@@ -203,6 +203,26 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments and result as pa_decode without the workspace, which
+ * is a 21 MiB array the library keeps on each GPU until the process ends
+ * (its address is looked up once per device; no hipMalloc, hipFree or
+ * other allocating call is made).  Its first 4 MiB hold the arrival
+ * counters (8 bytes per (sequence, KV head): num_seqs * num_kv_heads at
+ * most 524288), the other 17 MiB the partial results (2048 slots of
+ * G * (head_dim + 2) floats, G = num_q_heads / num_kv_heads: G * (head_dim
+ * + 2) at most 2176, e.g. G = 16 with head_dim 128).  The array starts
+ * zero-filled and every call leaves its counters back at zero.  All calls
+ * on one GPU share it, so calls that overlap on one GPU (different streams
+ * without ordering) race.  PA_ERR_UNSUPPORTED, with nothing launched, when
+ * the shape needs more than either region holds. */
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                            float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
+                            void* stream);
+
 /* Causal multi-query attention through the block tables: prefill and
  * chunked prefill [P1 body: prefill allocates and fills a prompt's blocks;
  * P3 Step 3: the prompt's tokens fill logical blocks mapped to scattered

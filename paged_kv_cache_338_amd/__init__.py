@@ -77,6 +77,8 @@ SIGNATURES = {
     "pa_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32, _c.c_float, _P, _I32, _PDESC,
                          _P, _c.c_size_t, _P]),
     "pa_decode_workspace_size": (_I32, [_PDESC, _I32, _I32, _I32, _c.POINTER(_c.c_size_t)]),
+    "pa_decode_noalloc": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32, _c.c_float, _P, _I32,
+                                 _PDESC, _P]),
     "pa_prefill": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _c.c_float, _P, _I32,
                           _PDESC, _P]),
     "pa_prefill_split": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _c.c_float, _P,
@@ -327,6 +329,29 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale
         int(block_size), float(scale), _dev(out, "out"), H_q, ctypes.byref(desc),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, block_size, scale, out,
+                      stream=None):
+    """pa_decode with the library's own per-GPU workspace (no allocation)."""
+    torch = _torch()
+    _same_pool(k_cache, v_cache)
+    desc = cache_desc(k_cache)
+    if q.dim() != 3 or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be [B, H_q, D] of one shape")
+    B, H_q, D = q.shape
+    if D != desc.head_dim or q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise ValueError("q/out must match the pool's head_dim and dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    _check(load_library().pa_decode_noalloc(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(context_lens, "context_lens"), B, int(block_size), float(scale), _dev(out, "out"),
+        H_q, ctypes.byref(desc), _stream(stream)))
     return out
 
 

@@ -69,6 +69,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "pa_attn_tile.h"
@@ -949,6 +950,40 @@ decode_kernel(DecodeArgs a) {
 // ----------------------------------------------------------- host helpers
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workspace of pa_decode_noalloc, for callers that cannot allocate (code
+// under HIP graph capture, tight serving loops): one array per GPU, held
+// until the process ends.  Fixed regions: the arrival counters in the first
+// 4 MiB (so no call's pieces ever land where another call's counters are),
+// the published pieces after them.  The array starts zero-filled (static
+// storage) and every call leaves its counters at zero, so it needs no
+// clearing.  All calls on one GPU share it: overlapping calls race.
+constexpr size_t kScratchCtrBytes = 4u << 20;
+constexpr size_t kScratchBytes = 21u << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device (its host-side name is
+// only a stand-in), looked up once per device.
+pa_status scratch_pointer(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return pa::fail(PA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return pa::fail(PA_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess)
+    return pa::fail(PA_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s",
+                    hipGetErrorString(g_scratch_err[dev]));
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 struct WorkspaceLayout {
   size_t o_off, ml_off, pieces_end, ctr_off, total;
 };
@@ -1133,6 +1168,39 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                        ws ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr,
                        ws ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr,
                        ws ? reinterpret_cast<uint64_t*>(ws + wl.ctr_off) : nullptr, stream);
+}
+
+pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                            float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
+                            void* stream) {
+  pa_status st = pa_supported(desc, num_q_heads);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_seqs > kMaxSeqs)
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "num_seqs %d outside [0, %d]", num_seqs, kMaxSeqs);
+  // The array's fixed regions: counters in [0, 4 MiB), pieces after.
+  const WorkspaceLayout wl = workspace_layout(desc, num_q_heads, num_seqs);
+  const size_t ctr_bytes = wl.total - wl.ctr_off;
+  if (ctr_bytes > kScratchCtrBytes || wl.pieces_end > kScratchBytes - kScratchCtrBytes)
+    return pa::fail(PA_ERR_UNSUPPORTED,
+                    "pa_decode_noalloc: this shape needs %zu bytes of counters (at most %zu) and "
+                    "%zu bytes of partial results (at most %zu) in its %zu-byte device array "
+                    "(use pa_decode with a workspace)",
+                    ctr_bytes, kScratchCtrBytes, wl.pieces_end, kScratchBytes - kScratchCtrBytes,
+                    kScratchBytes);
+  void* base = nullptr;
+  if (num_seqs > 0) {
+    st = scratch_pointer(&base);
+    if (st != PA_OK) return st;
+  }
+  char* ws = reinterpret_cast<char*>(base);
+  char* pieces = ws ? ws + kScratchCtrBytes : nullptr;
+  return decode_launch(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, block_size, scale, out, num_q_heads, desc,
+                       reinterpret_cast<float*>(pieces ? pieces + wl.o_off : nullptr),
+                       reinterpret_cast<float*>(pieces ? pieces + wl.ml_off : nullptr),
+                       reinterpret_cast<uint64_t*>(ws), stream);
 }
 
 }  // extern "C"
