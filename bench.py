@@ -98,7 +98,10 @@ def kv_bytes_per_token(w):
     return 2 * w.num_kv_heads * w.head_dim * (2 if w.dtype == "bf16" else 4)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_llama3_8b_batch8_hbm_traffic.txt")
+TRAFFIC_FILES = {
+    "llama3_8b_decode": os.path.join(ROOT, "profiles", "pa_decode_llama3_8b_batch8_hbm_traffic.txt"),
+    "serving_batch": os.path.join(ROOT, "profiles", "pa_decode_serving_batch_hbm_traffic.txt"),
+}
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_338_amd", "csrc", f)
                   for f in ("pa_decode.hip", "pa_attn_tile.h", "pa_device.h")]
 
@@ -114,11 +117,14 @@ def decode_source_hash():
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per pa_decode call from the committed counter summary, or None
-    when the decode code has changed since the counters were taken."""
+def measured_traffic(workload="llama3_8b_decode"):
+    """HBM bytes per pa_decode call on a workload from its committed counter
+    summary, or None when there is none or the decode code has changed since
+    the counters were taken."""
+    if workload not in TRAFFIC_FILES:
+        return None
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(TRAFFIC_FILES[workload]).read()
         code_hash = decode_source_hash()
     except OSError:
         return None
@@ -148,13 +154,23 @@ def oracle_decode_inputs(w):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, family, model and
+    stepping (which identify the part where the name is generic), and the
+    logical CPUs the host shows."""
+    first, n = {}, 0
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            k = k.strip()
+            if k == "processor":
+                n += 1
+            elif k in ("model name", "cpu family", "model", "stepping") and k not in first:
+                first[k] = v.strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    return (f"{first.get('model name', 'unknown')} (cpu family {first.get('cpu family', '?')}, "
+            f"model {first.get('model', '?')}, stepping {first.get('stepping', '?')}; "
+            f"{n} logical CPUs on the host)")
 
 
 def time_oracle_decode(w, inputs, seconds, threads):
@@ -176,29 +192,44 @@ def time_oracle_decode(w, inputs, seconds, threads):
 
 
 def cpu_baseline(w, seconds):
-    """The oracle (NumPy fp64) on one layer of the same batch, on every core
-    this process may use; plus one-thread passes of the same batch and of
-    the tiny reference batch."""
+    """The oracle (NumPy fp64) on one layer of the same batch: for 1 thread
+    and for every core this process may use, three trials of about
+    seconds / 6 each; per thread count the median of the trials' seconds
+    per pass, and the better thread count is the value.  Plus a one-thread
+    pass of the tiny reference batch."""
     import workloads as W
 
     cores = len(os.sched_getaffinity(0))
     inputs = oracle_decode_inputs(w)
     ntok = int(inputs[3].sum())
-    runs, el = time_oracle_decode(w, inputs, seconds, cores)
-    per = el / runs
-    gbs = ntok * kv_bytes_per_token(w) / per / 1e9
-    one = {}
-    for name, ww, inp, secs in (("llama3_8b_batch8", w, inputs, 2.0),
-                                ("tiny_ref", W.tiny_ref(), None, 1.0)):
-        inp = inp if inp is not None else oracle_decode_inputs(ww)
-        r1, e1 = time_oracle_decode(ww, inp, secs, 1)
-        one[name] = {"us_per_layer": round(e1 / r1 * 1e6, 1), "passes": r1,
-                     "GB/s": round(int(inp[3].sum()) * kv_bytes_per_token(ww) / (e1 / r1) / 1e9, 4)}
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+    kv = ntok * kv_bytes_per_token(w)
+    counts = sorted({1, cores})
+    per_threads = {}
+    for t in counts:
+        trials = [time_oracle_decode(w, inputs, seconds / (3 * len(counts)), t) for _ in range(3)]
+        per_pass = sorted(el / runs for runs, el in trials)
+        per_threads[t] = {"median_s_per_pass": per_pass[1],
+                          "trials_s_per_pass": [round(x, 5) for x in per_pass],
+                          "passes": [runs for runs, _ in trials]}
+    best = min(counts, key=lambda t: per_threads[t]["median_s_per_pass"])
+    per = per_threads[best]["median_s_per_pass"]
+    tw = W.tiny_ref()
+    tinp = oracle_decode_inputs(tw)
+    r1, e1 = time_oracle_decode(tw, tinp, 1.0, 1)
+    tiny = {"us_per_pass": round(e1 / r1 * 1e6, 1), "passes": r1,
+            "GB/s": round(int(tinp[3].sum()) * kv_bytes_per_token(tw) / (e1 / r1) / 1e9, 4)}
+    return {"value": round(kv / per / 1e9, 4), "unit": "GB/s", "cores": best, "kind": "oracle",
             "us_per_layer": round(per * 1e6, 1), "cpu_model": cpu_model(),
-            "one_thread": one,
-            "sample": f"{runs} full passes of one layer of the batch ({ntok} tokens) "
-                      f"in {el:.1f} s, NumPy fp64 paged decode incl. bf16 widening"}
+            "threads_tried": {str(t): {"GB/s": round(kv / v["median_s_per_pass"] / 1e9, 4),
+                                       "us_per_layer_median": round(v["median_s_per_pass"] * 1e6, 1),
+                                       "trials_s_per_pass": v["trials_s_per_pass"],
+                                       "passes": v["passes"]}
+                              for t, v in per_threads.items()},
+            "tiny_ref_one_thread": tiny,
+            "sample": f"one layer of the batch ({ntok} tokens, {kv} KV bytes), NumPy fp64 paged "
+                      f"decode incl. bf16 widening; 3 trials of about {seconds / (3 * len(counts)):.1f}"
+                      f" s per thread count in {counts}; value = median of the 3 at the faster "
+                      f"count ({best})"}
 
 
 def copy_calibration(mib):
@@ -234,6 +265,87 @@ def copy_bandwidth(dev, nbytes=1 << 30, reps=5):
     del src, dst
     return {"bytes": nbytes, "us": round(us, 1), "read_GBps": round(nbytes / us / 1e3, 1),
             "read_plus_write_GBps": round(2 * nbytes / us / 1e3, 1)}
+
+
+FLOOR_LIB = os.path.join(ROOT, "paged_kv_cache_338_amd", "libpa_floor.so")
+
+
+def decode_floor(kpool, vpool, tables_np, lens_np, w, reps, wgs=256):
+    """The decode call's cost floor on the same pools: graphs of one launch
+    per layer pool, replayed `reps` times between HIP events, of
+    * a read of every (block, KV head) tile the call reads, K and V, from a
+      precomputed offset list (no table walk, no arithmetic);
+    * a contiguous read of the same bytes (the K half from the K pool, the
+      V half from the V pool);
+    * an empty kernel (the per-launch cost of a back-to-back launch),
+    each over `wgs` workgroups of 256 threads, as the decode launches."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(FLOOR_LIB)
+    lib.pa_floor_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_floor_read_contiguous.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                             ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p,
+                                             ctypes.c_void_p]
+    lib.pa_floor_empty.argtypes = [ctypes.c_int32, ctypes.c_void_p]
+    tile = lib.pa_floor_tile_bytes()
+    H_kv, bs, D = w.num_kv_heads, w.block_size, w.head_dim
+    if bs * D * 2 != tile or w.dtype != "bf16":
+        raise SystemExit("decode_floor: only for bf16 pools with 16 x 128 tiles")
+    offs = [(int(tables_np[b, j]) * H_kv + h) * tile
+            for h in range(H_kv) for b in range(len(lens_np))
+            for j in range(-(-int(lens_np[b]) // bs))]
+    pool_bytes = kpool[0].numel() * kpool[0].element_size()
+    if max(offs) + tile > pool_bytes or len(offs) * tile > pool_bytes:
+        raise SystemExit("decode_floor: tile offsets outside the pools")
+    offs_d = torch.tensor(offs, dtype=torch.int64, device=kpool[0].device)
+    sink = torch.zeros(wgs * 256, dtype=torch.int32, device=kpool[0].device)
+    magic = 0x9E3779B9  # the XOR of the loaded words is never expected to hit it
+    n = len(offs)
+    per_pool = n * tile  # bytes read from each of K and V
+    nl = len(kpool)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"floor kernel launch failed: hipError {rc}")
+
+    def time_graph(launch):
+        stream = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            h = side.cuda_stream
+            for l in range(nl):
+                launch(l, h)
+            side.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                for l in range(nl):
+                    launch(l, h)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * nl)
+
+    tiles_us = time_graph(lambda l, h: check(lib.pa_floor_read_tiles(
+        kpool[l].data_ptr(), vpool[l].data_ptr(), offs_d.data_ptr(), n, wgs, magic,
+        sink.data_ptr(), h)))
+    contig_us = time_graph(lambda l, h: check(lib.pa_floor_read_contiguous(
+        kpool[l].data_ptr(), vpool[l].data_ptr(), per_pool, wgs, magic, sink.data_ptr(), h)))
+    empty_us = time_graph(lambda l, h: check(lib.pa_floor_empty(wgs, h)))
+    return {"tiles": n, "tile_bytes_each_of_k_and_v": tile, "bytes_read": 2 * n * tile,
+            "workgroups": wgs, "read_tiles_us": round(tiles_us, 3),
+            "read_contiguous_us": round(contig_us, 3), "empty_launch_us": round(empty_us, 3),
+            "timing": f"{reps} replays of a graph of {nl} launches, one per layer pool"}
 
 
 def replay_timed(make_calls, reps):
@@ -278,7 +390,7 @@ def replay_allocator_script(pa, w):
             alloc.seq_reserve(op[1], op[2], cow_cap=len(op[1]))
     maxb = max(len(alloc.seq_block_table(s)) for s in w.seq_ids)
     tables, lens = alloc.build_block_tables(w.seq_ids, maxb)
-    return tables, lens, maxb
+    return tables, lens, maxb, alloc
 
 
 def other_workload(args):
@@ -313,7 +425,7 @@ def other_workload(args):
     else:
         raise SystemExit(f"unknown workload {name}")
     dev = "cuda:0"
-    tables, lens, maxb = replay_allocator_script(pa, w)
+    tables, lens, maxb, alloc = replay_allocator_script(pa, w)
     B, H_q, D = w.batch, w.num_q_heads, w.head_dim
     shape = (w.num_blocks, w.num_kv_heads, w.block_size, D)
     gen = torch.Generator(device=dev).manual_seed(w.seed)
@@ -330,8 +442,13 @@ def other_workload(args):
                       args.kernel_reps) / args.layers
     kv = int(lens.sum()) * kv_bytes_per_token(w)
     gbs = kv / (us * 1e-6) / 1e9
+    # Tail waste: idle slots at the end of each sequence's last block (the
+    # blocks the allocator holds for the batch, less the tokens they hold).
+    held = w.num_blocks - alloc.num_free()
+    idle = held * w.block_size - int(lens.sum())
+    idle_pct = 100.0 * idle / (held * w.block_size)
     log(f"{args.workload}: B={B} tokens={int(lens.sum())} maxb={maxb}: {us:.2f} us/call, "
-        f"{gbs:.0f} GB/s")
+        f"{gbs:.0f} GB/s; {held} blocks held, {idle} idle slots ({idle_pct:.3f} %)")
     print(json.dumps({
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.kernel_reps * args.layers, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
@@ -340,9 +457,12 @@ def other_workload(args):
         "config": {"workload": f"{args.workload}: pa_decode alone, {args.layers} layer pools, "
                                "graph replay",
                    "batch": B, "tokens": int(lens.sum()), "block_size": w.block_size,
-                   "us_per_call": round(us, 3)},
+                   "us_per_call": round(us, 3), "blocks_held": held, "idle_slots": idle,
+                   "idle_slots_pct": round(idle_pct, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if f16 else measured_traffic(name),
+                     "kernel": "pa_decode (decode_kernel, one launch)",
                      "algorithmic_bytes_per_call": kv}}), flush=True)
 
 
@@ -592,7 +712,7 @@ def prefill_workload(args):
         raise SystemExit(f"unknown workload {name}")
     dev = "cuda:0"
     w = W.llama3_8b_decode(with_values=False)
-    tables, lens, maxb = replay_allocator_script(pa, w)
+    tables, lens, maxb, _ = replay_allocator_script(pa, w)
     nq = prefill_queries(lens, chunk)
     qs = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     T, H_q, D = int(qs[-1]), w.num_q_heads, w.head_dim
@@ -961,6 +1081,10 @@ def main():
         lambda: [pa.prepare_decode(q, kpool[0], vpool[0], tables_d, lens_d, bs, w.scale,
                                    outs[l], ws) for l in range(nl)]))
     log(f"pa_decode, one pool (MALL-warm): {us_warm:.2f} us/launch")
+    floor = decode_floor(kpool, vpool, tables_np, lens_np, w, args.kernel_reps)
+    log(f"floor: tile read {floor['read_tiles_us']:.2f} us, contiguous read "
+        f"{floor['read_contiguous_us']:.2f} us, empty launch {floor['empty_launch_us']:.2f} us "
+        f"({floor['tiles']} tiles)")
 
     # ---- whole decode steps
     new_k = to_dev(w.notes["new_k"], w.dtype, dev)
@@ -1053,10 +1177,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "traffic_note": "HBM bytes per call (both kernels) from FETCH_SIZE/WRITE_SIZE "
-                                     "counter passes scaled by a copy of known size; null when the "
+                     "traffic_note": "HBM bytes per call from FETCH_SIZE/WRITE_SIZE counter "
+                                     "passes scaled by a copy of known size; null when the "
                                      "decode sources changed since",
-                     "kernel": "pa_decode (split + merge kernels), one layer, "
+                     "kernel": "pa_decode (decode_kernel, one launch), one layer, "
                                f"{int(lens_np.sum())} tokens x 4096 B",
                      "us_per_launch": round(us_launch, 3),
                      "us_per_launch_median": round(p50, 3), "us_per_launch_p10": round(p10, 3),
@@ -1065,6 +1189,8 @@ def main():
                                f"one per layer pool; mean over all {launches} calls, median and "
                                "p10/p90 of the per-replay means",
                      "mall_warm_us_per_launch": round(us_warm, 3),
+                     "floor_us": floor["read_tiles_us"],
+                     "floor": floor,
                      "algorithmic_bytes_per_call": kv_launch},
     }
     cb = copy_bandwidth(dev)

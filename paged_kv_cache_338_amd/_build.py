@@ -1,6 +1,8 @@
 """Builds libpa.so in-tree: host C++ with g++, device code with hipcc (gfx950).
 
 Run as ``python -m paged_kv_cache_338_amd._build``.  Always recompiles.
+It also builds ``libpa_floor.so``, the benchmark's floor kernels (a separate
+library: nothing in libpa.so uses them).
 
 ``python -m paged_kv_cache_338_amd._build --sanitize`` builds a second copy,
 ``libpa_sanitize.so``, whose host sources (the allocator and the status
@@ -33,6 +35,9 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 SANITIZE_LIB = os.path.join(PKG, "libpa_sanitize.so")
+# Measurement kernels for the decode's cost floor, loaded by bench.py only.
+FLOOR_LIB = os.path.join(PKG, "libpa_floor.so")
+FLOOR_SOURCE = "pa_floor.hip"
 
 ARCH = "gfx950"
 HOST_SOURCES = ["pa_status.cpp", "pa_allocator.cpp"]
@@ -86,7 +91,19 @@ def build(verbose: bool = True) -> str:
     tmp = LIB + ".tmp"
     _run([_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    build_floor(verbose)
     return LIB
+
+
+def build_floor(verbose: bool = True) -> str:
+    """libpa_floor.so: the benchmark's floor kernels (not part of libpa.so)."""
+    os.makedirs(OBJ, exist_ok=True)
+    obj = os.path.join(OBJ, FLOOR_SOURCE + ".o")
+    _run([_hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, FLOOR_SOURCE), "-o", obj], verbose)
+    tmp = FLOOR_LIB + ".tmp"
+    _run([_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", obj, "-o", tmp], verbose)
+    os.replace(tmp, FLOOR_LIB)
+    return FLOOR_LIB
 
 
 def build_sanitize(verbose: bool = True) -> str:

@@ -21,3 +21,12 @@ def page_figures():
     import json
     with open(os.path.join(HERE, "golden", "page_figures.json")) as f:
         return json.load(f)
+
+
+def pytest_terminal_summary(terminalreporter):
+    import parity_log
+    lines = parity_log.summary_lines()
+    if lines:
+        terminalreporter.section("parity: measured max-abs errors")
+        for line in lines:
+            terminalreporter.write_line(line)

@@ -12,6 +12,7 @@ import os
 import numpy as np
 import pytest
 
+import parity_log
 import workloads as W
 from oracle import attention as oatt
 from oracle import cache_ops as ocops
@@ -43,9 +44,7 @@ def assert_close(w, got_t, want, tol=None):
     got = _gd().widen_out(got_t, w.dtype)
     assert got.shape == want.shape
     assert np.isfinite(got).all()
-    err = float(np.abs(got - want).max())
-    assert err <= (TOL[w.dtype] if tol is None else tol), err
-    return err
+    return parity_log.within(got, want, TOL[w.dtype] if tol is None else tol, w.dtype, w.name)
 
 
 def assert_pools_equal(w, gc, oc):
@@ -115,6 +114,7 @@ def test_block_size_sweep(bs):
     w = W.block_size_sweep(bs, with_values=False)
     w.q, w.k_rows, w.v_rows = base.q, base.k_rows, base.v_rows
     oc, gc = run_both(w)
+    assert_pools_equal(w, gc, oc)
     assert_close(w, gc.decode(), oc.decode())
 
 
@@ -156,11 +156,17 @@ SHAPES = [
     (2, 2, 64, 4, "f32", [1, 4, 5, 63, 64]),
     (4, 2, 128, 16, "f32", [16, 17, 100]),
     (4, 1, 64, 2, "f32", [9, 3]),
+    (3, 2, 128, 32, "f32", [1, 31, 32, 33, 300]),
+    (8, 1, 128, 128, "f32", [1, 127, 128, 129, 400]),
+    (16, 1, 128, 256, "f32", [255, 256, 257, 600]),
+    (3, 2, 64, 16, "f32", [17, 90]),
     (4, 2, 128, 16, "f16", [1, 15, 16, 17, 31, 32, 33, 200]),
     (8, 1, 64, 8, "f16", [5, 130, 64]),
     (4, 2, 128, 4, "f16", [3, 4, 77]),
     (16, 1, 128, 32, "f16", [300, 1]),
     (4, 8, 128, 16, "f16", [128, 700, 1500, 300]),
+    (3, 2, 128, 16, "f16", [50, 51, 1, 333]),
+    (3, 1, 64, 32, "f16", [31, 32, 33, 97]),
 ]
 
 
@@ -227,7 +233,7 @@ def test_one_context_of_131072_tokens():
     got = _direct_decode(q, k, v, tables, lens, 16, scale, "bf16")
     want = oatt.paged_decode(q, k, v, tables, lens, 16, scale, "bf16")
     assert np.isfinite(got).all()
-    assert float(np.abs(got - want).max()) <= TOL["bf16"]
+    parity_log.within(got, want, TOL["bf16"], "bf16")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -246,7 +252,7 @@ def test_maximum_batch_of_8192_sequences(dtype):
     got = _direct_decode(q, k, v, tables, lens, 16, scale, dtype)
     assert np.isfinite(got).all()
     assert np.array_equal(got[lens == 0], np.zeros_like(got[lens == 0]))
-    assert float(np.abs(got - want).max()) <= TOL[dtype]
+    parity_log.within(got, want, TOL[dtype], dtype)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

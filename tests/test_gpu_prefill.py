@@ -7,6 +7,7 @@ shows up as a non-finite or wrong output."""
 import numpy as np
 import pytest
 
+import parity_log
 import workloads as W
 from oracle import prefill as opf
 
@@ -90,8 +91,7 @@ def _compare(q, k, v, t, lens, qs, bs, scale, dtype="bf16"):
     want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, dtype)
     assert got.shape == want.shape
     assert np.isfinite(got).all()
-    err = float(np.abs(got - want).max()) if got.size else 0.0
-    assert err <= TOL[dtype], err
+    err = parity_log.within(got, want, TOL[dtype], dtype)
     return got
 
 
@@ -142,7 +142,7 @@ def test_one_query_token_matches_decode():
                  torch.from_numpy(lens).to(dev), bs, scale, out)
     torch.cuda.synchronize()
     dec = out.cpu().to(torch.float64).numpy()
-    assert float(np.abs(got - dec).max()) <= TOL["bf16"]
+    parity_log.within(got, dec, TOL["bf16"], "bf16")
 
 
 def test_physical_relabelling_is_bit_identical():
@@ -295,8 +295,7 @@ def _check_split(seed, lengths, nq, dtype="bf16", **kw):
     got = _run_split(q, k, v, t, lens, qs, bs, scale, dtype, reps=2)
     want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, dtype)
     assert np.isfinite(got).all()
-    err = float(np.abs(got - want).max()) if got.size else 0.0
-    assert err <= TOL[dtype], err
+    err = parity_log.within(got, want, TOL[dtype], dtype)
     return got
 
 
@@ -323,9 +322,9 @@ def test_split_llama_shape_chunk64():
     got = _run_split(q, k, v, t, lens, qs, bs, scale, reps=2)
     want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "bf16")
     assert np.isfinite(got).all()
-    assert float(np.abs(got - want).max()) <= TOL["bf16"]
+    parity_log.within(got, want, TOL["bf16"], "bf16")
     whole = _run(q, k, v, t, lens, qs, bs, scale)
-    assert float(np.abs(got - whole).max()) <= TOL["bf16"]
+    parity_log.within(got, whole, TOL["bf16"], "bf16")
 
 
 def test_split_rising_logits(key_tiles_knob):
@@ -342,7 +341,7 @@ def test_split_rising_logits(key_tiles_knob):
     scale = 1.0 / np.sqrt(128)
     got = _run_split(q, k, v, t, lens, qs, bs, scale)
     want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "bf16")
-    assert float(np.abs(got - want).max()) <= TOL["bf16"]
+    parity_log.within(got, want, TOL["bf16"], "bf16")
 
 
 def test_split_f16_and_negative_scale(key_tiles_knob):
@@ -352,7 +351,7 @@ def test_split_f16_and_negative_scale(key_tiles_knob):
     for scale in (1.0 / 8, -1.0 / 8):
         got = _run_split(q, k, v, t, lens, qs, bs, scale, "f16")
         want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "f16")
-        assert float(np.abs(got - want).max()) <= TOL["f16"]
+        parity_log.within(got, want, TOL["f16"], "f16")
 
 
 def test_split_not_taken_for_many_query_blocks():
@@ -386,8 +385,7 @@ def _sampled_rows_match(got, q, k, v, t, lens, qs, bs, scale, per_seq, seed):
             pos.append(int(lens[b]) - n + i)
             seq.append(b)
     want = oatt.paged_decode(q[rows], k, v, t[seq], np.array(pos) + 1, bs, scale, "bf16")
-    err = float(np.abs(got[rows] - want).max())
-    assert err <= TOL["bf16"], err
+    err = parity_log.within(got[rows], want, TOL["bf16"], "bf16")
     return len(rows)
 
 
@@ -454,7 +452,7 @@ def test_split_graph_replay_matches_eager():
     call(out_e)
     torch.cuda.synchronize()
     want = opf.paged_prefill(q, k, v, t, lens, qs, bs, scale, "bf16")
-    assert float(np.abs(out_e.cpu().to(torch.float64).numpy() - want).max()) <= TOL["bf16"]
+    parity_log.within(out_e.cpu().to(torch.float64).numpy(), want, TOL["bf16"], "bf16")
     # The same rows with the second sequence's chunk cut to its last 20 tokens.
     qs2 = qs.copy()
     qs2[2:] -= 44

@@ -6,6 +6,7 @@ oracle's causal attention over the whole prompt (needs a gfx950 GPU)."""
 import numpy as np
 import pytest
 
+import parity_log
 import workloads as W
 from oracle import prefill as opf
 
@@ -89,4 +90,4 @@ def test_cached_prefix_then_suffix_prefill_matches_oracle():
     v_np = vc.cpu().view(torch.int16).numpy().view(np.uint16)
     want = opf.paged_prefill(q, k_np, v_np, tables, lens, qs_np, BS, 1 / np.sqrt(D), "bf16")
     assert np.isfinite(got).all()
-    assert float(np.abs(got - want).max()) <= 2e-2
+    parity_log.within(got, want, 2e-2, "bf16")

@@ -12,6 +12,7 @@ block ids.
 import numpy as np
 import pytest
 
+import parity_log
 import workloads as W
 from oracle import cache_ops as ocops
 from oracle_driver import OracleCache
@@ -135,7 +136,7 @@ def test_swap_out_and_in_round_trip_is_bit_exact():
     got = gc.decode(q=w.q[rest], tables=t, lens=l)
     oc = OracleCache(w).run()
     want = oc.decode()[rest]
-    assert float(np.abs(gd.widen_out(got, "bf16") - want).max()) <= 2e-2
+    parity_log.within(gd.widen_out(got, "bf16"), want, 2e-2, "bf16")
     # Make room, swap back in (other device blocks), decode everything.
     gc.alloc.seq_free(99)
     for s in (6, 4):

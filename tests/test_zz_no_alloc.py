@@ -9,6 +9,7 @@ the array is rejected."""
 import numpy as np
 import pytest
 
+import parity_log
 import workloads as W
 from oracle_driver import OracleCache
 
@@ -41,8 +42,7 @@ def _check(w, sl):
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16), want_ws.view(torch.int16))
     want = oc.decode()[sl]
-    err = float(np.abs(gd.widen_out(got, w.dtype) - want).max())
-    assert err <= TOL[w.dtype], err
+    err = parity_log.within(gd.widen_out(got, w.dtype), want, TOL[w.dtype], w.dtype)
     return err
 
 
