@@ -117,10 +117,10 @@ def decode_source_hash():
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
-def measured_traffic(workload="llama3_8b_decode"):
-    """HBM bytes per pa_decode call on a workload from its committed counter
-    summary, or None when there is none or the decode code has changed since
-    the counters were taken."""
+def measured_traffic(workload="llama3_8b_decode", key="traffic_bytes_per_call"):
+    """HBM bytes per call (the `key` line) on a workload from its committed
+    counter summary, or None when there is none or the decode code has
+    changed since the counters were taken."""
     if workload not in TRAFFIC_FILES:
         return None
     try:
@@ -128,11 +128,10 @@ def measured_traffic(workload="llama3_8b_decode"):
         code_hash = decode_source_hash()
     except OSError:
         return None
-    fields = dict(line.split(": ", 1) for line in text.splitlines()
-                  if line.startswith(("kernel_source_sha256: ", "traffic_bytes_per_call: ")))
-    if fields.get("kernel_source_sha256") != code_hash:
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line)
+    if fields.get("kernel_source_sha256") != code_hash or key not in fields:
         return None
-    return int(fields["traffic_bytes_per_call"])
+    return int(fields[key])
 
 
 def oracle_decode_inputs(w):
@@ -437,9 +436,14 @@ def other_workload(args):
     ws = pa.decode_workspace(kp[0], B, H_q, maxb)
     td = torch.from_numpy(tables).to(dev)
     ld = torch.from_numpy(lens).to(dev)
-    us = replay_timed(lambda: [pa.prepare_decode(q, kp[l], vp[l], td, ld, w.block_size, w.scale,
-                                                 outs[l], ws) for l in range(args.layers)],
-                      args.kernel_reps) / args.layers
+    # A graph of 32 calls cycling over the layer pools (as the default leg's
+    # 32 layers), so the gap between graph replays is spread over 32 calls.
+    ncalls = 32
+    us = replay_timed(lambda: [pa.prepare_decode(q, kp[c % args.layers], vp[c % args.layers], td,
+                                                 ld, w.block_size, w.scale,
+                                                 outs[c % args.layers], ws)
+                               for c in range(ncalls)],
+                      args.kernel_reps) / ncalls
     kv = int(lens.sum()) * kv_bytes_per_token(w)
     gbs = kv / (us * 1e-6) / 1e9
     # Tail waste: idle slots at the end of each sequence's last block (the
@@ -451,11 +455,11 @@ def other_workload(args):
         f"{gbs:.0f} GB/s; {held} blocks held, {idle} idle slots ({idle_pct:.3f} %)")
     print(json.dumps({
         "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.kernel_reps * args.layers, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
+        "steps": args.kernel_reps * ncalls, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if f16 else "bf16", "data": "synthetic",
-        "config": {"workload": f"{args.workload}: pa_decode alone, {args.layers} layer pools, "
-                               "graph replay",
+        "config": {"workload": f"{args.workload}: pa_decode alone, graph replay of {ncalls} "
+                               f"calls cycling over {args.layers} layer pools",
                    "batch": B, "tokens": int(lens.sum()), "block_size": w.block_size,
                    "us_per_call": round(us, 3), "blocks_held": held, "idle_slots": idle,
                    "idle_slots_pct": round(idle_pct, 3)},
@@ -742,7 +746,7 @@ def prefill_workload(args):
         f"{us:.2f} us/call, {tfs:.1f} TFLOP/s")
     result = {
         "metric": PREFILL_METRIC, "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.kernel_reps * args.layers, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
+        "steps": args.kernel_reps * ncalls, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if f16 else "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload}: pa_prefill alone, {args.layers} layer pools, "
@@ -995,6 +999,9 @@ def main():
     B, L0 = w.batch, w.context_lens.copy()
     H_q, H_kv, D, bs = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     nl = args.layers
+    if args.warmup < 1:
+        args.warmup = 1  # the first step captures the layer loop
+        log("--warmup raised to 1: the first step captures the layer loop")
     total_steps = args.warmup + args.steps
     maxb = int(math.ceil((L0.max() + total_steps + 1) / bs))
     log(f"workload {w.name}: B={B} tokens={int(L0.sum())} layers={nl} pool={w.num_blocks} "
@@ -1027,10 +1034,10 @@ def main():
     torch.cuda.synchronize()
     log("prefill done")
 
-    # ---- roofline leg: pa_decode alone, back-to-back over the layer pools.
-    # The calls only enqueue kernels (no allocation, no memset), so they are
-    # captured once in a HIP graph and replayed: the timing is then the
-    # GPU's, not Python's launch rate.
+    # ---- decode-only leg: pa_decode alone, back-to-back over the layer
+    # pools, on the prefilled cache.  The calls only enqueue kernels (no
+    # allocation, no memset), so they are captured once in a HIP graph and
+    # replayed: the timing is then the GPU's, not Python's launch rate.
     stream = torch.cuda.current_stream()
 
     def captured(make_calls):
@@ -1068,13 +1075,13 @@ def main():
         per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.kernel_reps)])
         return evs[0].elapsed_time(evs[-1]) * 1e3 / (args.kernel_reps * nl), per * 1e3 / nl
 
-    us_launch, per_rep = timed_replays(run_dec)
-    p10, p50, p90 = (float(x) for x in np.percentile(per_rep, [10, 50, 90]))
+    us_dec, per_rep = timed_replays(run_dec)
+    d10, d50, d90 = (float(x) for x in np.percentile(per_rep, [10, 50, 90]))
     launches = args.kernel_reps * nl
-    kv_launch = int(lens_np.sum()) * kv_bytes_per_token(w)
-    achieved = kv_launch / (us_launch * 1e-6) / 1e9
-    log(f"pa_decode: {us_launch:.2f} us/launch (median {p50:.2f}, p10 {p10:.2f}, p90 {p90:.2f}), "
-        f"{achieved:.0f} GB/s over {launches} launches")
+    kv_dec = int(lens_np.sum()) * kv_bytes_per_token(w)
+    achieved_dec = kv_dec / (us_dec * 1e-6) / 1e9
+    log(f"pa_decode alone: {us_dec:.2f} us/launch (median {d50:.2f}, p10 {d10:.2f}, p90 {d90:.2f}), "
+        f"{achieved_dec:.0f} GB/s over {launches} launches")
     # The same calls all on layer 0's pools: the 268 MB pair then stays in
     # the 256 MB last-level cache in large part (labelled MALL-warm).
     us_warm, _ = timed_replays(captured(
@@ -1086,7 +1093,9 @@ def main():
         f"{floor['read_contiguous_us']:.2f} us, empty launch {floor['empty_launch_us']:.2f} us "
         f"({floor['tiles']} tiles)")
 
-    # ---- whole decode steps
+    # ---- whole decode steps.  Per layer one pa_decode_append call: the
+    # new token's K and V are written at position L - 1 (its slot from the
+    # table) and the layer's attention runs, in one kernel.
     new_k = to_dev(w.notes["new_k"], w.dtype, dev)
     new_v = to_dev(w.notes["new_v"], w.dtype, dev)
     pin = [dict(slots=torch.empty(B, dtype=torch.int64, pin_memory=True),
@@ -1094,20 +1103,16 @@ def main():
                 lens=torch.empty(B, dtype=torch.int32, pin_memory=True),
                 pairs=torch.empty((B, 2), dtype=torch.int32, pin_memory=True),
                 ev=torch.cuda.Event()) for _ in range(2)]
-    slots_d = torch.empty(B, dtype=torch.int64, device=dev)
     pairs_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
 
     def layer_calls():
-        calls = []
-        for l in range(nl):
-            calls.append(pa.prepare_cache_append(new_k, new_v, slots_d, kpool[l], vpool[l]))
-            calls.append(pa.prepare_decode(q, kpool[l], vpool[l], tables_d, lens_d, bs, w.scale,
-                                           outs[l], ws))
-        return calls
+        return [pa.prepare_decode_append(q, new_k, new_v, kpool[l], vpool[l], tables_d, lens_d, bs,
+                                         w.scale, outs[l], ws) for l in range(nl)]
 
     seq_ids = np.array(w.seq_ids, np.int64)
     ones = np.ones(B, np.int32)
     kv_read = []
+    last_lens = np.zeros(B, np.int32)
 
     def step(i):
         buf = pin[i % 2]
@@ -1119,22 +1124,25 @@ def main():
             buf["pairs"].numpy()[:npairs] = p
         alloc.build_block_tables(seq_ids, maxb, tables_out=buf["tables"].numpy(),
                                  lens_out=buf["lens"].numpy())
-        slots_d.copy_(buf["slots"], non_blocking=True)
         tables_d.copy_(buf["tables"], non_blocking=True)
         lens_d.copy_(buf["lens"], non_blocking=True)
         if npairs:
             pairs_d[:npairs].copy_(buf["pairs"][:npairs], non_blocking=True)
         buf["ev"].record(stream)
         kv_read.append(int(buf["lens"].numpy().sum()) * kv_bytes_per_token(w) * nl)
+        last_lens[:] = buf["lens"].numpy()
         if npairs:  # copy-on-write before the step's appends (none in this batch)
             for l in range(nl):
                 pa.prepare_copy_blocks(pairs_d, npairs, kpool[l], vpool[l])()
-        run_layers()
+        nonlocal run_layers
+        if run_layers is None:
+            run_layers = captured(layer_calls)
+        else:
+            run_layers()
 
-    # The device uploads of the first step happen before capture so that the
-    # captured appends write real slots (replays write the step's own).
-    slots_d.fill_(-1)  # capture-time eager run: every append slot skipped
-    run_layers = captured(layer_calls)
+    # The first (warm-up) step captures the layer loop: the capture's eager
+    # run is that step's work, after its uploads; later steps replay.
+    run_layers = None
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -1159,6 +1167,20 @@ def main():
         f"p10 {sp10:.3f}, p90 {sp90:.3f}, max {step_ms.max():.3f} ms; wall {wall * 1e3:.1f} ms, "
         f"GPU {gpu_ms:.1f} ms), {value:.0f} GB/s")
 
+    # ---- roofline leg: the step's kernel, pa_decode_append, on the last
+    # step's tables and lengths, back-to-back over the layer pools (each
+    # replay writes the same new rows again and decodes).
+    run_app = captured(lambda: [pa.prepare_decode_append(q, new_k, new_v, kpool[l], vpool[l],
+                                                         tables_d, lens_d, bs, w.scale, outs[l],
+                                                         ws) for l in range(nl)])
+    us_launch, per_rep = timed_replays(run_app)
+    p10, p50, p90 = (float(x) for x in np.percentile(per_rep, [10, 50, 90]))
+    kv_launch = int(last_lens.sum()) * kv_bytes_per_token(w)
+    alg_launch = kv_launch + B * kv_bytes_per_token(w)  # + the new rows written
+    achieved = alg_launch / (us_launch * 1e-6) / 1e9
+    log(f"pa_decode_append: {us_launch:.2f} us/launch (median {p50:.2f}, p10 {p10:.2f}, "
+        f"p90 {p90:.2f}), {achieved:.0f} GB/s over {launches} launches")
+
     mode = "eager launches" if args.eager else "HIP graph replay of the layer loop"
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -1166,9 +1188,10 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "llama3_8b_decode: per step, host slot reservation + table upload, "
-                               f"then {nl} layers x (pa_cache_append + pa_decode) by {mode}; "
-                               "32 Q / 8 KV heads, head 128, bs 16, bf16, pool 4096 blocks "
-                               "per layer",
+                               f"then {nl} layers x pa_decode_append (the new token's K/V "
+                               f"written at its slot and the layer's decode, one kernel) by "
+                               f"{mode}; 32 Q / 8 KV heads, head 128, bs 16, bf16, pool 4096 "
+                               "blocks per layer",
                    "batch": B, "context_lens_at_first_step": (L0 + args.warmup + 1).tolist(),
                    "tokens_added_per_step": B, "layers": nl,
                    "us_per_layer": round(ms_step * 1e3 / nl, 3),
@@ -1180,18 +1203,30 @@ def main():
                      "traffic_note": "HBM bytes per call from FETCH_SIZE/WRITE_SIZE counter "
                                      "passes scaled by a copy of known size; null when the "
                                      "decode sources changed since",
-                     "kernel": "pa_decode (decode_kernel, one launch), one layer, "
-                               f"{int(lens_np.sum())} tokens x 4096 B",
+                     "kernel": "pa_decode_append (decode_kernel with the newest token's "
+                               "append, one launch), one layer: "
+                               f"{int(last_lens.sum())} tokens x 4096 B read + {B} x 4096 B "
+                               "written",
                      "us_per_launch": round(us_launch, 3),
                      "us_per_launch_median": round(p50, 3), "us_per_launch_p10": round(p10, 3),
                      "us_per_launch_p90": round(p90, 3),
-                     "timing": f"{args.kernel_reps} replays of a graph of {nl} pa_decode calls, "
-                               f"one per layer pool; mean over all {launches} calls, median and "
-                               "p10/p90 of the per-replay means",
-                     "mall_warm_us_per_launch": round(us_warm, 3),
-                     "floor_us": floor["read_tiles_us"],
-                     "floor": floor,
-                     "algorithmic_bytes_per_call": kv_launch},
+                     "timing": f"{args.kernel_reps} replays of a graph of {nl} pa_decode_append "
+                               f"calls, one per layer pool; mean over all {launches} calls, "
+                               "median and p10/p90 of the per-replay means",
+                     "algorithmic_bytes_per_call": alg_launch,
+                     "decode_only": {
+                         "kernel": "pa_decode alone on the prefilled cache, one layer, "
+                                   f"{int(lens_np.sum())} tokens x 4096 B",
+                         "us_per_launch": round(us_dec, 3),
+                         "us_per_launch_median": round(d50, 3),
+                         "us_per_launch_p10": round(d10, 3), "us_per_launch_p90": round(d90, 3),
+                         "achieved": round(achieved_dec, 1),
+                         "frac": round(achieved_dec / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(key="decode_only_traffic_bytes_per_call"),
+                         "algorithmic_bytes_per_call": kv_dec,
+                         "mall_warm_us_per_launch": round(us_warm, 3),
+                         "floor_us": floor["read_tiles_us"],
+                         "floor": floor}},
     }
     cb = copy_bandwidth(dev)
     result["roofline"]["copy_1gib"] = cb

@@ -203,6 +203,29 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Appends each sequence's newest token and attends over the result, in one
+ * kernel launch: "What is paged attention in vLLM, and why does it
+ * matter?", Step 4 (a generated token's K and V go to the next slot of the
+ * sequence's last block) followed by Step 3 (attention reads every position
+ * through the block table).  The result equals pa_cache_append of the B
+ * rows at the slots of positions L_b - 1 (slot = table[b][(L_b - 1) / bs]
+ * * bs + (L_b - 1) % bs), then pa_decode with the same arguments: the pools
+ * hold the same bytes and the output is bit-identical.
+ * new_k, new_v: device [num_seqs][num_kv_heads][head_dim], pool dtype,
+ *               16-byte aligned: K and V of the token at position L_b - 1
+ *               of sequence b (context_lens counts it).  A sequence with
+ *               L_b = 0 appends nothing; a block id outside the pool is
+ *               read clamped (output unspecified, as for pa_decode) and
+ *               nothing is written there.
+ * k_cache, v_cache: written at those slots only (the caller has done any
+ *               copy-on-write first, so each written block is private).
+ * Every other argument, the workspace and the errors as for pa_decode. */
+pa_status pa_decode_append(const void* q, const void* new_k, const void* new_v, void* k_cache,
+                           void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                           float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* pa_decode for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation):
  * the same arguments and result as pa_decode without the workspace, which

@@ -77,6 +77,8 @@ SIGNATURES = {
     "pa_decode": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32, _c.c_float, _P, _I32, _PDESC,
                          _P, _c.c_size_t, _P]),
     "pa_decode_workspace_size": (_I32, [_PDESC, _I32, _I32, _I32, _c.POINTER(_c.c_size_t)]),
+    "pa_decode_append": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _c.c_float, _P,
+                                _I32, _PDESC, _P, _c.c_size_t, _P]),
     "pa_decode_noalloc": (_I32, [_P, _P, _P, _P, _I32, _P, _I32, _I32, _c.c_float, _P, _I32,
                                  _PDESC, _P]),
     "pa_prefill": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _c.c_float, _P, _I32,
@@ -329,6 +331,41 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, block_size, scale
         int(block_size), float(scale), _dev(out, "out"), H_q, ctypes.byref(desc),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def _check_new_rows(new_k, new_v, k_cache, B):
+    shape = (B, k_cache.shape[1], k_cache.shape[3])
+    for name, t in (("new_k", new_k), ("new_v", new_v)):
+        if tuple(t.shape) != shape or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must be [B, H_kv, D] = {list(shape)} of the pool's dtype")
+
+
+def pa_decode_append(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, block_size,
+                     scale, out, workspace=None, stream=None):
+    """Writes new_k[b] / new_v[b] ([B, H_kv, D]) at position context_lens[b] - 1
+    of sequence b (its slot from block_tables), then decodes as pa_decode,
+    in one kernel launch."""
+    torch = _torch()
+    _same_pool(k_cache, v_cache)
+    desc = cache_desc(k_cache)
+    if q.dim() != 3 or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be [B, H_q, D] of one shape")
+    B, H_q, D = q.shape
+    if D != desc.head_dim or q.dtype != k_cache.dtype or out.dtype != k_cache.dtype:
+        raise ValueError("q/out must match the pool's head_dim and dtype")
+    _check_new_rows(new_k, new_v, k_cache, B)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    maxb = block_tables.shape[1]
+    if workspace is None:
+        workspace = decode_workspace(k_cache, B, H_q, maxb)
+        if stream is not None and stream != torch.cuda.current_stream():
+            workspace.record_stream(stream)
+    prepare_decode_append(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens,
+                          block_size, scale, out, workspace, stream)()
     return out
 
 
@@ -637,6 +674,25 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, block_size, 
             _stream(stream))
     return PreparedCall(lib.pa_decode, args, (q, k_cache, v_cache, block_tables, context_lens,
                                               out, workspace, desc))
+
+
+def prepare_decode_append(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens,
+                          block_size, scale, out, workspace, stream=None):
+    """pa_decode_append with its arguments fixed (see pa_decode_append)."""
+    _same_pool(k_cache, v_cache)
+    desc = cache_desc(k_cache)
+    B, H_q, _ = q.shape
+    _check_new_rows(new_k, new_v, k_cache, B)
+    maxb = block_tables.shape[1]
+    lib = load_library()
+    args = (_dev(q, "q"), _dev(new_k, "new_k"), _dev(new_v, "new_v"), _dev(k_cache, "k_cache"),
+            _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), maxb,
+            _dev(context_lens, "context_lens"), B, int(block_size), ctypes.c_float(scale),
+            _dev(out, "out"), H_q, ctypes.byref(desc), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    return PreparedCall(lib.pa_decode_append, args, (q, new_k, new_v, k_cache, v_cache,
+                                                     block_tables, context_lens, out, workspace,
+                                                     desc))
 
 
 def prepare_cache_append(k, v, slot_mapping, k_cache, v_cache, stream=None):

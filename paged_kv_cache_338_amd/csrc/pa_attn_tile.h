@@ -122,10 +122,16 @@ __device__ __forceinline__ void issue_tile(TileRegs<k16, D>& r, const KvPool& a,
 // lane reads its own rows' blocks.  Rows past the context length L (and
 // padding tiles, whose index the caller clamps) read the last valid token
 // again.
+//
+// new_row >= 0: row new_row of the tile is read from nk / nv (the first byte
+// of the new token's K and V rows) instead of the pools (see
+// issue_tile_with_row).
 template <bool k16, int D>
 __device__ __forceinline__ void issue_tile_small(TileRegs<k16, D>& r, const KvPool& a,
                                                  int32_t phys_v, int32_t jl, int32_t t,
-                                                 int32_t kvh, int32_t L, int nbt, int lane) {
+                                                 int32_t kvh, int32_t L, int nbt, int lane,
+                                                 int32_t new_row = -1, const char* nk = nullptr,
+                                                 const char* nv = nullptr) {
   using Geo = Geometry<k16, D>;
   const int bs_log = a.log2_bs;
   const int32_t bs = 1 << bs_log;
@@ -139,12 +145,17 @@ __device__ __forceinline__ void issue_tile_small(TileRegs<k16, D>& r, const KvPo
     return reinterpret_cast<const char*>(base) +
            (((int64_t)phys * a.H_kv + kvh) * bs + (tok & (bs - 1))) * Geo::kRowBytes;
   };
-  const char* kp = row_addr(lane & 15, a.k_cache) + jr * 16;
+  // The pool addresses are formed in every lane before any lane takes the
+  // new row instead: row_addr's shuffle reads other lanes, which must all be
+  // active.
+  const char* kc = row_addr(lane & 15, a.k_cache);
+  const char* kp = (c16 == new_row ? nk : kc) + jr * 16;
 #pragma unroll
   for (int p = 0; p < Geo::kKPieces; ++p) r.k[p] = *reinterpret_cast<const u32x4_t*>(kp + p * 64);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const char* vp = row_addr(jr * 4 + q, a.v_cache) + c16 * (Geo::kVWords * 4);
+    const char* vc = row_addr(jr * 4 + q, a.v_cache);
+    const char* vp = (jr * 4 + q == new_row ? nv : vc) + c16 * (Geo::kVWords * 4);
 #pragma unroll
     for (int h = 0; h < Geo::kVWords; h += 4) {
       if constexpr (Geo::kVWords >= 4) {
@@ -157,6 +168,50 @@ __device__ __forceinline__ void issue_tile_small(TileRegs<k16, D>& r, const KvPo
         uint2 x = *reinterpret_cast<const uint2*>(vp);
         r.v[q][0] = x.x;
         r.v[q][1] = x.y;
+      }
+    }
+  }
+}
+
+// For the tile that holds a sequence's newest token (written to the pools
+// by the same launch), after issue_tile: row new_row of the tile is loaded
+// again, from the token's own K and V rows (nk, nv: their first bytes),
+// into the lanes that hold that row, so the result does not depend on when
+// the write lands.  Buffer loads like issue_tile's, so they return after
+// the pool's loads into the same registers.
+template <bool k16, int D>
+__device__ __forceinline__ void reload_new_row(TileRegs<k16, D>& r, int32_t new_row,
+                                               const char* nk, const char* nv, int lane) {
+  using Geo = Geometry<k16, D>;
+  const int jr = lane >> 4, c16 = lane & 15;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(nk), 0, Geo::kRowBytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(nv), 0, Geo::kRowBytes, kRsrcWord3);
+  if (c16 == new_row) {
+#pragma unroll
+    for (int p = 0; p < Geo::kKPieces; ++p)
+      r.k[p] = __builtin_bit_cast(u32x4_t,
+                                  __builtin_amdgcn_raw_buffer_load_b128(rk, jr * 16 + p * 64, 0, 0));
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (jr * 4 + q == new_row) {
+      const int32_t vo = c16 * (Geo::kVWords * 4);
+#pragma unroll
+      for (int h = 0; h < Geo::kVWords; h += 4) {
+        if constexpr (Geo::kVWords >= 4) {
+          const u32x4_t x = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, vo + h * 4, 0, 0));
+          r.v[q][h + 0] = x[0];
+          r.v[q][h + 1] = x[1];
+          r.v[q][h + 2] = x[2];
+          r.v[q][h + 3] = x[3];
+        } else {
+          const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vo, 0, 0));
+          r.v[q][0] = x.x;
+          r.v[q][1] = x.y;
+        }
       }
     }
   }

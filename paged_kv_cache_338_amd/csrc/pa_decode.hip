@@ -104,6 +104,9 @@ constexpr int kDeviceScope = 16;
 #ifndef PA_DECODE_NB_BF16
 #define PA_DECODE_NB_BF16 3  // tiles per batch for 16-bit pools (build-time tuning knob)
 #endif
+#ifndef PA_DECODE_NB_APPEND
+#define PA_DECODE_NB_APPEND 2  // the same when appending (its new-row reloads need registers)
+#endif
 
 struct DecodeArgs {
   const void* q;
@@ -116,6 +119,8 @@ struct DecodeArgs {
   float* ws_ml;       // [2 * kMaxWGs][G][2] their reference max (log2 units) and sum
                       // of exp2(x - max), side by side so one 8-byte load fetches both
   uint64_t* counters;  // [H_kv * B] arrival counters, zero between calls
+  const void* new_k;   // pa_decode_append: [B][H_kv][D] rows of each sequence's newest
+  const void* new_v;   // token (position L - 1), written to the pools; else NULL
   int32_t B;
   int32_t max_blocks;
   int32_t num_blocks;
@@ -357,7 +362,7 @@ struct LdsPieces {
   int32_t flag[2];         // per published piece: 0 not last, 1 merge from L2, 2 at device scope
 };
 
-template <int E, int D, int GP, int NBUF, bool kSmall>
+template <int E, int D, int GP, int NBUF, bool kSmall, bool kAppend>
 __global__ void __launch_bounds__(kWG)
 __attribute__((amdgpu_waves_per_eu(kSmall ? (((E != 0) || GP * D < 16 * 128) ? 2 : 1)
                                           : ((E != 0) ? 2 : 1))))
@@ -420,6 +425,47 @@ decode_kernel(DecodeArgs a) {
     }
   }
   if (Tt == 0) return;
+
+  if constexpr (kAppend) {
+    // ---- the newest tokens' rows into the pools, spread over the waves of
+    // the grid at its start: pair p = (sequence b, KV head) goes to wave p
+    // mod W, 16 bytes per lane (K rows in the first half of a pair's lanes,
+    // V rows in the second).  The waves that read these rows take them from
+    // new_k / new_v, so nothing in this launch waits for the writes.
+    constexpr int kChunks = Geo::kRowBytes / 16;               // per row
+    constexpr int kPairsPerPass = kWave / (2 * kChunks) > 0 ? kWave / (2 * kChunks) : 1;
+    constexpr int kLanesPerPair = 2 * kChunks > kWave ? kWave : 2 * kChunks;
+    const int32_t npairs = B * H_kv, W = nwg * kNW;
+    const int32_t gw = bx * kNW + v;
+    const int pl = lane % kLanesPerPair;      // lane within its pair
+    const int pk = lane / kLanesPerPair;      // pair within the pass
+    for (int32_t p0 = gw * kPairsPerPass; p0 < npairs; p0 += W * kPairsPerPass) {
+      const int32_t p = p0 + pk;
+      if (p < npairs && pk < kPairsPerPass) {
+        const int32_t b = p / H_kv, kvh = p - b * H_kv;
+        const int32_t L = Ls[b];
+        if (L > 0) {
+          const int32_t e = min((L - 1) >> a.log2_bs, a.max_blocks - 1);
+          const int32_t phys = a.tables[(int64_t)b * a.max_blocks + e];
+          if (phys >= 0 && phys < a.num_blocks) {
+            const int64_t dst = ((((int64_t)phys * H_kv + kvh) << a.log2_bs) +
+                                 ((L - 1) & ((1 << a.log2_bs) - 1))) * Geo::kRowBytes;
+            const int64_t src = (int64_t)p * Geo::kRowBytes;
+            // One row per half of the pair's lanes; rows of more than 64
+            // chunks (none here) would need more lanes.
+            for (int c = pl; c < 2 * kChunks; c += kLanesPerPair) {
+              const bool isv = c >= kChunks;
+              const int off = (isv ? c - kChunks : c) * 16;
+              const char* sp = reinterpret_cast<const char*>(isv ? a.new_v : a.new_k) + src + off;
+              char* dp = reinterpret_cast<char*>(const_cast<void*>(isv ? a.v_cache : a.k_cache)) +
+                         dst + off;
+              *reinterpret_cast<u32x4_t*>(dp) = *reinterpret_cast<const u32x4_t*>(sp);
+            }
+          }
+        }
+      }
+    }
+  }
 
   // ---- shares.  Logical workgroup lw takes share [T*lw/W, T*(lw+1)/W);
   // with W a multiple of 8 the workgroups with blockIdx = x mod 8 (one XCD)
@@ -604,6 +650,21 @@ decode_kernel(DecodeArgs a) {
         for (int u = 0; u < NBUF; ++u) {
           int32_t kvh, t;
           slot_tile(bt, u, kvh, t);
+          if constexpr (kAppend) {
+            // The tile holding a segment's newest token (its last tile)
+            // reads that row from the token's own rows.
+            const bool inA = u < bt.nA;
+            const int32_t S1 = inA ? bt.A.S1 : bt.B.S1, L = inA ? bt.A.L : bt.B.L;
+            const int32_t b = inA ? bt.A.b : bt.B.b;
+            issue_tile<BF16, D>(buf[u], a.pool(), ph[u], t, kvh, lane, u < bt.n);
+            if (u < bt.n && bt.fa + u == S1 - 1) {  // uniform
+              const int64_t src = ((int64_t)b * H_kv + kvh) * Geo::kRowBytes;
+              pa::reload_new_row<BF16, D>(buf[u], (L - 1) & (kTile - 1),
+                                          reinterpret_cast<const char*>(a.new_k) + src,
+                                          reinterpret_cast<const char*>(a.new_v) + src, lane);
+            }
+            continue;
+          }
           issue_tile<BF16, D>(buf[u], a.pool(), ph[u], t, kvh, lane, u < bt.n);
         }
         const Batch nx = next();
@@ -682,6 +743,16 @@ decode_kernel(DecodeArgs a) {
             dA = dB;
             chunkA = c;
             dB = describe(c + 1);
+          }
+          if constexpr (kAppend) {
+            if (j < n && t0 + jj == s.nt - 1) {  // uniform: the segment's last tile
+              const int64_t src = ((int64_t)s.b * H_kv + s.kvh) * Geo::kRowBytes;
+              issue_tile_small<BF16, D>(r, a.pool(), dA, jj - (c << tpc_log), t0 + jj, s.kvh, s.L,
+                                        nbt, lane, (s.L - 1) & (kTile - 1),
+                                        reinterpret_cast<const char*>(a.new_k) + src,
+                                        reinterpret_cast<const char*>(a.new_v) + src);
+              return;
+            }
           }
           issue_tile_small<BF16, D>(r, a.pool(), dA, jj - (c << tpc_log), t0 + jj, s.kvh, s.L, nbt,
                                     lane);
@@ -1007,8 +1078,9 @@ WorkspaceLayout workspace_layout(const pa_cache_desc* d, int32_t H_q, int32_t B)
 
 // Tiles per batch.  fp32 pools with large query groups hold G*D/16 output
 // floats per lane in registers, which leaves room for one tile per batch.
-template <bool k16, int D, int GP>
-constexpr int kNbuf = k16 ? (GP >= 8 ? 2 : PA_DECODE_NB_BF16) : (GP * D >= 8 * 64 ? 1 : 2);
+template <bool k16, int D, int GP, bool kAppend>
+constexpr int kNbuf = k16 ? (GP >= 8 ? 2 : (kAppend ? PA_DECODE_NB_APPEND : PA_DECODE_NB_BF16))
+                          : (GP * D >= 8 * 64 ? 1 : 2);
 
 template <int D, int GP>
 size_t lds_bytes(int32_t B) {
@@ -1017,9 +1089,11 @@ size_t lds_bytes(int32_t B) {
 
 template <int E, int D, int GP>
 pa_status launch(const DecodeArgs& a, int wgs, hipStream_t s) {
-  constexpr int NBUF = kNbuf<(E != 0), D, GP>;
-  auto kern = a.log2_bs >= 4 ? decode_kernel<E, D, GP, NBUF, false>
-                             : decode_kernel<E, D, GP, NBUF, true>;
+  constexpr int NB = kNbuf<(E != 0), D, GP, false>, NBA = kNbuf<(E != 0), D, GP, true>;
+  auto kern = a.new_k ? (a.log2_bs >= 4 ? decode_kernel<E, D, GP, NBA, false, true>
+                                        : decode_kernel<E, D, GP, NBA, true, true>)
+                      : (a.log2_bs >= 4 ? decode_kernel<E, D, GP, NB, false, false>
+                                        : decode_kernel<E, D, GP, NB, true, false>);
   const size_t lds = lds_bytes<D, GP>(a.B);
   if (lds > kMaxLds)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: %d sequences need %zu bytes of LDS (> %zu)",
@@ -1085,7 +1159,8 @@ pa_status decode_launch(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_tables, int32_t max_blocks_per_seq,
                         const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
                         float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
-                        float* ws_o, float* ws_ml, uint64_t* counters, void* stream) {
+                        float* ws_o, float* ws_ml, uint64_t* counters, void* stream,
+                        const void* new_k = nullptr, const void* new_v = nullptr) {
   pa_status st = pa_supported(desc, num_q_heads);
   if (st != PA_OK) return st;
   if (block_size != desc->block_size)
@@ -1124,6 +1199,8 @@ pa_status decode_launch(const void* q, const void* k_cache, const void* v_cache,
   a.counters = counters;
   a.ws_o = ws_o;
   a.ws_ml = ws_ml;
+  a.new_k = new_k;
+  a.new_v = new_v;
   a.B = num_seqs;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = desc->num_blocks;
@@ -1168,6 +1245,35 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                        ws ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr,
                        ws ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr,
                        ws ? reinterpret_cast<uint64_t*>(ws + wl.ctr_off) : nullptr, stream);
+}
+
+pa_status pa_decode_append(const void* q, const void* new_k, const void* new_v, void* k_cache,
+                           void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                           float scale, void* out, int32_t num_q_heads, const pa_cache_desc* desc,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status st = pa_supported(desc, num_q_heads);
+  if (st != PA_OK) return st;
+  if (num_seqs > 0 && (!new_k || !new_v))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "NULL pointer");
+  if (!pa::aligned(new_k, 16) || !pa::aligned(new_v, 16))
+    return pa::fail(PA_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  char* ws = reinterpret_cast<char*>(workspace);
+  WorkspaceLayout wl{};
+  if (num_seqs > 0 && num_seqs <= kMaxSeqs && ws) {
+    if (!pa::aligned(workspace, 256))
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+    wl = workspace_layout(desc, num_q_heads, num_seqs);
+    if (workspace_bytes < wl.total)
+      return pa::fail(PA_ERR_INVALID_ARGUMENT, "workspace %zu bytes < %zu needed",
+                      workspace_bytes, wl.total);
+  }
+  return decode_launch(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, block_size, scale, out, num_q_heads, desc,
+                       ws ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr,
+                       ws ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr,
+                       ws ? reinterpret_cast<uint64_t*>(ws + wl.ctr_off) : nullptr, stream,
+                       num_seqs > 0 ? new_k : nullptr, num_seqs > 0 ? new_v : nullptr);
 }
 
 pa_status pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,

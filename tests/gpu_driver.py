@@ -44,8 +44,11 @@ class GpuCache:
         self.v_rows = to_torch(w.v_rows, w.dtype, device) if upload_rows else None
         self.log = []
 
-    def run(self, script=None):
+    def run(self, script=None, skip_rows=()):
+        """Replays the script; bank rows in skip_rows are reserved but not
+        appended (their slots are passed as -1)."""
         w = self.w
+        skip = set(int(r) for r in skip_rows)
         for op in (w.script if script is None else script):
             if op[0] == "create":
                 self.alloc.seq_create(op[1])
@@ -58,9 +61,12 @@ class GpuCache:
                     pa.pa_copy_blocks(torch.from_numpy(np.ascontiguousarray(pairs)).to(self.device),
                                       self.k_cache, self.v_cache)
                 idx = torch.from_numpy(np.asarray(rows, np.int64)).to(self.device)
+                aslots = slots.copy()
+                if skip:
+                    aslots[[int(r) in skip for r in rows]] = -1
                 pa.pa_cache_append(self.k_rows.index_select(0, idx).contiguous(),
                                    self.v_rows.index_select(0, idx).contiguous(),
-                                   torch.from_numpy(slots.copy()).to(self.device),
+                                   torch.from_numpy(aslots).to(self.device),
                                    self.k_cache, self.v_cache)
                 self.log.append((slots.copy(), pairs.copy()))
         torch.cuda.synchronize()

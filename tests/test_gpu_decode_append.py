@@ -1,0 +1,294 @@
+"""pa_decode_append (append each sequence's newest token and decode, in one
+launch) against the oracle's append followed by its decode (needs a GPU).
+
+The GPU side replays each workload's script with every sequence's last
+token reserved but not appended (NaN-poisoned slots), then calls
+pa_decode_append with those tokens' rows.  The pools must then equal the
+oracle's bit for bit, the output must be within the decode tolerance of the
+oracle's, and bit-identical to pa_decode on the now complete pools.
+"""
+
+import numpy as np
+import pytest
+
+import parity_log
+import workloads as W
+from oracle_driver import OracleCache
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 6e-3}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import paged_kv_cache_338_amd as pa
+    pa.load_library()
+    yield
+
+
+def _small(seed, lengths, G=4, H_kv=2, D=128, bs=16, dtype="bf16", spare=3):
+    rng = np.random.default_rng(seed)
+    nb = sum(-(-L // bs) for L in lengths) + spare
+    free_order = rng.permutation(nb).astype(np.int32)
+    mk = lambda *s: W._normal(rng, s, dtype)
+    q = mk(len(lengths), G * H_kv, D)
+    k = mk(max(1, sum(lengths)), H_kv, D)
+    v = mk(max(1, sum(lengths)), H_kv, D)
+    script, logical = W._sequential_script(lengths)
+    return W.Workload("small", seed, G * H_kv, H_kv, D, bs, dtype, 1.0 / np.sqrt(D), nb,
+                      free_order, q, k, v, script, list(range(len(lengths))), logical)
+
+
+def _new_rows(w):
+    """Bank rows of each sequence's newest token (row 0 for empty ones)."""
+    return np.array([int(r[-1]) if len(r) else 0 for r in w.logical_rows], np.int64)
+
+
+def run_fused(w, tables=None, lens=None, wgs=None):
+    """(oracle cache, GPU cache, fused output, pa_decode output afterwards)."""
+    import torch
+
+    import gpu_driver as gd
+    import paged_kv_cache_338_amd as pa
+
+    oc = OracleCache(w).run()
+    last = [int(r[-1]) for r in w.logical_rows if len(r)]
+    gc = gd.GpuCache(w).run(skip_rows=last)
+    if tables is None:
+        tables, lens = gc.tables()
+    dev = gc.device
+    idx = torch.from_numpy(_new_rows(w)).to(dev)
+    nk = gc.k_rows.index_select(0, idx).contiguous()
+    nv = gc.v_rows.index_select(0, idx).contiguous()
+    qd = gd.to_torch(w.q, w.dtype, dev)
+    td = torch.from_numpy(np.ascontiguousarray(tables, np.int32)).to(dev)
+    ld = torch.from_numpy(np.ascontiguousarray(lens, np.int32)).to(dev)
+    out = torch.full_like(qd, float("nan"))
+    if wgs is None:
+        pa.pa_decode_append(qd, nk, nv, gc.k_cache, gc.v_cache, td, ld, w.block_size, w.scale,
+                            out)
+    else:
+        with pa.tuning(pa.PA_TUNE_DECODE_WORKGROUPS, wgs):
+            pa.pa_decode_append(qd, nk, nv, gc.k_cache, gc.v_cache, td, ld, w.block_size,
+                                w.scale, out)
+    torch.cuda.synchronize()
+    # pa_decode on the now complete pools, with the same grid.
+    after = torch.full_like(qd, float("nan"))
+    with pa.tuning(pa.PA_TUNE_DECODE_WORKGROUPS, 0 if wgs is None else wgs):
+        pa.pa_decode(qd, gc.k_cache, gc.v_cache, td, ld, w.block_size, w.scale, after)
+    torch.cuda.synchronize()
+    return oc, gc, out, after
+
+
+def check(w, **kw):
+    import gpu_driver as gd
+
+    oc, gc, out, after = run_fused(w, **kw)
+    assert np.array_equal(gd.to_numpy(gc.k_cache, w.dtype).view(np.uint8),
+                          np.ascontiguousarray(oc.k_cache).view(np.uint8))
+    assert np.array_equal(gd.to_numpy(gc.v_cache, w.dtype).view(np.uint8),
+                          np.ascontiguousarray(oc.v_cache).view(np.uint8))
+    got = gd.widen_out(out, w.dtype)
+    assert np.isfinite(got).all()
+    parity_log.within(got, oc.decode(), TOL[w.dtype], w.dtype, w.name)
+    assert np.array_equal(gd.to_numpy(out, w.dtype), gd.to_numpy(after, w.dtype))
+    return got
+
+
+def test_tiny_ref():
+    check(W.tiny_ref())
+
+
+def test_llama3_8b_batch():
+    check(W.llama3_8b_decode())
+
+
+def test_serving_batch():
+    check(W.serving_batch())
+
+
+@pytest.mark.parametrize("bs", [8, 128])
+def test_block_size_sweep(bs):
+    base = W.block_size_sweep(8)
+    w = W.block_size_sweep(bs, with_values=False)
+    w.q, w.k_rows, w.v_rows = base.q, base.k_rows, base.v_rows
+    check(w)
+
+
+def test_prefix_sharing_after_copy_on_write():
+    check(W.prefix_sharing(prefix_len=2056))
+
+
+SHAPES = [
+    # (G, H_kv, D, bs, dtype, lengths): newest token first, last, mid-block,
+    # at a tile boundary, in a block smaller than a tile, empty sequences
+    (4, 2, 128, 16, "bf16", [1, 15, 16, 17, 31, 32, 33, 200]),
+    (1, 3, 128, 16, "bf16", [0, 5, 40, 0, 100]),
+    (2, 2, 64, 8, "bf16", [7, 8, 9, 130]),
+    (8, 1, 128, 32, "bf16", [1, 33, 64, 65, 500]),
+    (16, 1, 128, 16, "bf16", [300, 3]),
+    (3, 2, 128, 16, "bf16", [50, 51]),
+    (4, 2, 128, 4, "bf16", [3, 4, 5, 77]),
+    (4, 2, 128, 1, "bf16", [1, 2, 19]),
+    (4, 2, 128, 2, "bf16", [1, 2, 3, 33]),
+    (4, 2, 128, 256, "bf16", [255, 256, 257]),
+    (2, 2, 64, 4, "f32", [1, 4, 5, 63, 64]),
+    (4, 2, 128, 16, "f32", [16, 17, 100]),
+    (4, 1, 64, 2, "f32", [9, 3]),
+    (16, 1, 128, 32, "f32", [31, 32, 33, 70]),
+    (8, 1, 128, 8, "f32", [9, 16, 17]),
+    (4, 2, 128, 16, "f16", [1, 15, 16, 17, 31, 32, 33, 200]),
+    (8, 1, 64, 8, "f16", [5, 130, 64]),
+    (3, 2, 128, 4, "f16", [3, 4, 77]),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"G{s[0]}_H{s[1]}_D{s[2]}_bs{s[3]}_{s[4]}"
+                                               for s in SHAPES])
+def test_shapes(shape):
+    G, H_kv, D, bs, dtype, lengths = shape
+    check(_small(23, lengths, G, H_kv, D, bs, dtype))
+
+
+@pytest.mark.parametrize("wgs", [1, 3, 97, 1024])
+def test_grid_sizes(wgs):
+    """Any grid: pools bit-exact, output within tolerance of the oracle and
+    bit-identical to pa_decode on the same grid."""
+    check(W.llama3_8b_decode(), wgs=wgs)
+
+
+def test_block_outside_the_pool_writes_nothing():
+    """A newest token whose block id lies outside the pool: nothing is
+    written for it (the pools keep their NaN there), every other sequence
+    is appended and decoded as usual."""
+    import torch
+
+    import gpu_driver as gd
+    import paged_kv_cache_338_amd as pa
+
+    w = _small(29, [20, 35, 7], G=4, H_kv=2, D=128, bs=16)
+    oc = OracleCache(w).run()
+    last = [int(r[-1]) for r in w.logical_rows]
+    gc = gd.GpuCache(w).run(skip_rows=last)
+    tables, lens = gc.tables()
+    k_before = gd.to_numpy(gc.k_cache, w.dtype).copy()
+    bad = 1  # sequence 1's newest token (position 34) is in its block 2
+    tables = tables.copy()
+    tables[bad, 34 // 16] = w.num_blocks + 5
+    dev = gc.device
+    idx = torch.from_numpy(_new_rows(w)).to(dev)
+    nk = gc.k_rows.index_select(0, idx).contiguous()
+    nv = gc.v_rows.index_select(0, idx).contiguous()
+    qd = gd.to_torch(w.q, w.dtype, dev)
+    out = torch.empty_like(qd)
+    pa.pa_decode_append(qd, nk, nv, gc.k_cache, gc.v_cache, torch.from_numpy(tables).to(dev),
+                        torch.from_numpy(lens).to(dev), w.block_size, w.scale, out)
+    torch.cuda.synchronize()
+    k_after = gd.to_numpy(gc.k_cache, w.dtype)
+    ok = np.ones(w.batch, bool)
+    ok[bad] = False
+    # Every row written is one of the other sequences' newest tokens.
+    changed = np.argwhere((k_after != k_before).any(axis=-1))
+    want = set()
+    otab, _ = oc.tables()
+    for b in np.flatnonzero(ok):
+        L = int(lens[b])
+        for h in range(w.num_kv_heads):
+            want.add((int(otab[b, (L - 1) // 16]), h, (L - 1) % 16))
+    assert {tuple(int(x) for x in c) for c in changed} == want
+    got = gd.widen_out(out, w.dtype)
+    ref = oc.decode()
+    parity_log.within(got[ok], ref[ok], TOL[w.dtype], w.dtype, "block outside the pool")
+
+
+def test_rejects_bad_new_rows():
+    import torch
+
+    import paged_kv_cache_338_amd as pa
+
+    w = _small(31, [5, 9], G=2, H_kv=2, D=64, bs=16)
+    import gpu_driver as gd
+    gc = gd.GpuCache(w).run()
+    tables, lens = gc.tables()
+    dev = gc.device
+    qd = gd.to_torch(w.q, w.dtype, dev)
+    out = torch.empty_like(qd)
+    td, ld = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    good = torch.zeros((2, 2, 64), dtype=qd.dtype, device=dev)
+    with pytest.raises(ValueError):
+        pa.pa_decode_append(qd, good[:, :1], good, gc.k_cache, gc.v_cache, td, ld, 16, 0.125, out)
+    with pytest.raises(ValueError):
+        pa.pa_decode_append(qd, good.float(), good, gc.k_cache, gc.v_cache, td, ld, 16, 0.125, out)
+
+
+def test_graph_replay_appends_and_decodes_each_step():
+    """The fused call captured once and replayed for three steps, the
+    lengths, tables and new rows changed between replays: each replay
+    matches the oracle's append + decode of that step."""
+    import torch
+
+    import gpu_driver as gd
+    import paged_kv_cache_338_amd as pa
+
+    w = W.llama3_8b_decode()
+    oc = OracleCache(w).run()
+    gc = gd.GpuCache(w).run()
+    dev = gc.device
+    B, maxb = w.batch, 300
+    rng = np.random.default_rng(77)
+    qd = gd.to_torch(w.q, w.dtype, dev)
+    out = torch.empty_like(qd)
+    td = torch.zeros((B, maxb), dtype=torch.int32, device=dev)
+    ld = torch.zeros(B, dtype=torch.int32, device=dev)
+    nk = torch.empty((B, w.num_kv_heads, w.head_dim), dtype=qd.dtype, device=dev)
+    nv = torch.empty_like(nk)
+    ws = pa.decode_workspace(gc.k_cache, B, w.num_q_heads, maxb)
+
+    def stage():
+        # One new token per sequence: both allocators reserve, the oracle
+        # appends, the GPU gets the rows for the fused call.
+        rows_k = W._normal(rng, (B, w.num_kv_heads, w.head_dim), w.dtype)
+        rows_v = W._normal(rng, (B, w.num_kv_heads, w.head_dim), w.dtype)
+        so, po = oc.alloc.seq_reserve(w.seq_ids, [1] * B)
+        sg, pg = gc.alloc.seq_reserve(w.seq_ids, [1] * B, cow_cap=B)
+        assert list(so) == sg.tolist() and len(po) == 0 and len(pg) == 0
+        from oracle import cache_ops as ocops
+        ocops.cache_append(oc.k_cache, oc.v_cache, rows_k, rows_v, so, w.block_size)
+        t, l = gc.alloc.build_block_tables(w.seq_ids, maxb)
+        td.copy_(torch.from_numpy(t))
+        ld.copy_(torch.from_numpy(l))
+        nk.copy_(gd.to_torch(rows_k, w.dtype, dev))
+        nv.copy_(gd.to_torch(rows_v, w.dtype, dev))
+        torch.cuda.synchronize()
+
+    stage()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        # Prepared on the capture stream (a prepared call keeps its stream).
+        call = pa.prepare_decode_append(qd, nk, nv, gc.k_cache, gc.v_cache, td, ld,
+                                        w.block_size, w.scale, out, ws)
+        call()  # eager step 1
+        side.synchronize()
+        got = gd.widen_out(out, w.dtype)
+        parity_log.within(got, oc.decode(), TOL["bf16"], "bf16", "eager step")
+        with torch.cuda.graph(g, stream=side):
+            call()
+    torch.cuda.synchronize()
+    # The capture ran nothing; step 1's append already happened, so
+    # replaying it again writes the same bytes.
+    for step in range(3):
+        if step:
+            stage()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(gd.to_numpy(gc.k_cache, w.dtype).view(np.uint8),
+                              np.ascontiguousarray(oc.k_cache).view(np.uint8))
+        assert np.array_equal(gd.to_numpy(gc.v_cache, w.dtype).view(np.uint8),
+                              np.ascontiguousarray(oc.v_cache).view(np.uint8))
+        got = gd.widen_out(out, w.dtype)
+        parity_log.within(got, oc.decode(), TOL["bf16"], "bf16", f"replay {step}")
