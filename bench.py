@@ -746,7 +746,7 @@ def prefill_workload(args):
         f"{us:.2f} us/call, {tfs:.1f} TFLOP/s")
     result = {
         "metric": PREFILL_METRIC, "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.kernel_reps * ncalls, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
+        "steps": args.kernel_reps * args.layers, "warmup": 1, "ms_per_step": round(us / 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if f16 else "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload}: pa_prefill alone, {args.layers} layer pools, "
