@@ -446,11 +446,14 @@ def other_workload(args):
                       args.kernel_reps) / ncalls
     kv = int(lens.sum()) * kv_bytes_per_token(w)
     gbs = kv / (us * 1e-6) / 1e9
-    # Tail waste: idle slots at the end of each sequence's last block (the
-    # blocks the allocator holds for the batch, less the tokens they hold).
+    # Tail waste: idle slots at the end of each sequence's last block,
+    # ceil(L / bs) bs - L summed over the sequences, as a share of their
+    # table slots (blocks shared by several sequences count once per
+    # sequence here; blocks_held counts each once).
     held = w.num_blocks - alloc.num_free()
-    idle = held * w.block_size - int(lens.sum())
-    idle_pct = 100.0 * idle / (held * w.block_size)
+    slots = int(sum(-(-int(L) // w.block_size) * w.block_size for L in lens))
+    idle = slots - int(lens.sum())
+    idle_pct = 100.0 * idle / slots
     log(f"{args.workload}: B={B} tokens={int(lens.sum())} maxb={maxb}: {us:.2f} us/call, "
         f"{gbs:.0f} GB/s; {held} blocks held, {idle} idle slots ({idle_pct:.3f} %)")
     print(json.dumps({
