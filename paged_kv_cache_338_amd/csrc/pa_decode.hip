@@ -104,6 +104,9 @@ constexpr int kDeviceScope = 16;
 #ifndef PA_DECODE_NB_BF16
 #define PA_DECODE_NB_BF16 3  // tiles per batch for 16-bit pools (build-time tuning knob)
 #endif
+#ifndef PA_DECODE_MERGE_BATCH
+#define PA_DECODE_MERGE_BATCH 8  // contributors' loads in flight per lane in the merge
+#endif
 #ifndef PA_DECODE_NB_APPEND
 #define PA_DECODE_NB_APPEND 2  // the same when appending (its new-row reloads need registers)
 #endif
@@ -958,7 +961,7 @@ decode_kernel(DecodeArgs a) {
         const int32_t mine = piece(i0 + min(sub, cn - 1));
         const f32x2_t ml = __builtin_bit_cast(
             f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rml, (mine * G + g) * 8, 0, 0));
-        constexpr int kBatch = 16;  // output loads in flight per lane
+        constexpr int kBatch = PA_DECODE_MERGE_BATCH;  // output loads in flight per lane
         for (int32_t u0 = 0; u0 < cn; u0 += kBatch) {
           floatx4_t po[kBatch];
 #pragma unroll

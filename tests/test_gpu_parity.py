@@ -160,6 +160,8 @@ SHAPES = [
     (8, 1, 128, 128, "f32", [1, 127, 128, 129, 400]),
     (16, 1, 128, 256, "f32", [255, 256, 257, 600]),
     (3, 2, 64, 16, "f32", [17, 90]),
+    (8, 1, 128, 16, "f32", [1, 16, 17, 250]),
+    (16, 1, 64, 32, "f32", [31, 33, 200]),
     (4, 2, 128, 16, "f16", [1, 15, 16, 17, 31, 32, 33, 200]),
     (8, 1, 64, 8, "f16", [5, 130, 64]),
     (4, 2, 128, 4, "f16", [3, 4, 77]),
