@@ -97,17 +97,25 @@ const char* pa_last_error(void);
 pa_status pa_supported(const pa_cache_desc* desc, int32_t num_q_heads);
 
 /* Process-wide tuning knobs.  Each changes only how work is spread over
- * the GPU, never the result beyond fp32 summation order; 0 (the default)
- * lets the library choose.  Read by every later call of the operation
- * (atomically; any thread may set them).
+ * the GPU or how it uses the caches, never the result beyond fp32
+ * summation order; 0 (the default) lets the library choose.  Read by every
+ * later call of the operation (atomically; any thread may set them).
  *   PA_TUNE_DECODE_WORKGROUPS: workgroups of pa_decode's grid, in
  *     [1, 1024] (default 256, one per compute unit).
  *   PA_TUNE_PREFILL_KEY_TILES: key tiles of 32 keys per piece when
  *     pa_prefill_split splits (default: from the shape, at least 48).
+ *   PA_TUNE_DECODE_KV_CACHED: 0 (default): pa_decode / pa_decode_append
+ *     read K and V with non-temporal loads (each block is read once per
+ *     call, so keeping it in the caches only evicts what the call reuses);
+ *     1: ordinary cached loads, for batches whose sequences share blocks
+ *     ("What is paged attention in vLLM, and why does it matter?",
+ *     Trade-offs, fourth point: a shared prefix is read by every sharer in
+ *     the same call and is then served from the caches).
  * INVALID_ARGUMENT for an unknown key or a value out of range. */
 typedef int32_t pa_tuning_key;
 #define PA_TUNE_DECODE_WORKGROUPS 1
 #define PA_TUNE_PREFILL_KEY_TILES 2
+#define PA_TUNE_DECODE_KV_CACHED 3
 pa_status pa_set_tuning(pa_tuning_key key, int32_t value);
 pa_status pa_get_tuning(pa_tuning_key key, int32_t* value);
 

@@ -33,6 +33,7 @@ PA_BF16 = 1
 PA_F16 = 2
 PA_TUNE_DECODE_WORKGROUPS = 1
 PA_TUNE_PREFILL_KEY_TILES = 2
+PA_TUNE_DECODE_KV_CACHED = 3
 
 STATUS_NAMES = {PA_ERR_INVALID_ARGUMENT: "INVALID_ARGUMENT", PA_ERR_OUT_OF_BLOCKS: "OUT_OF_BLOCKS",
                 PA_ERR_UNKNOWN_SEQ: "UNKNOWN_SEQ", PA_ERR_UNSUPPORTED: "UNSUPPORTED",

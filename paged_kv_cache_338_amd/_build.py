@@ -70,13 +70,20 @@ def _run(cmd, verbose):
 
 
 def _device_objects(verbose):
+    """Compiles the device sources concurrently (the decode source, with its
+    many kernel variants, takes minutes on its own)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     hipcc = _hipcc()
-    objs = []
+    jobs = []
     for src in DEVICE_SOURCES:
         obj = os.path.join(OBJ, src + ".o")
-        _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
-    return objs
+        jobs.append(([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj],
+                     obj))
+    with ThreadPoolExecutor(max_workers=len(jobs)) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd, _ in jobs]:
+            f.result()
+    return [obj for _, obj in jobs]
 
 
 def build(verbose: bool = True) -> str:

@@ -60,6 +60,10 @@ __device__ __forceinline__ char* uniform_ptr(const char* p) {
   return reinterpret_cast<char*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// Cache-policy operand of the buffer loads: non-temporal (the loaded lines
+// are the first the caches give up), for data read once per launch.
+constexpr int kNonTemporal = 2;
+
 // Buffer-resource word 3 for raw dword loads on gfx9-family parts (32-bit
 // data format; a zero format would make every load return zero).
 constexpr int32_t kRsrcWord3 = 0x00020000;
@@ -70,10 +74,12 @@ constexpr int32_t kRsrcWord3 = 0x00020000;
 // (`valid` false) gets a zero-length resource, so its loads return zeros
 // without touching memory.  Rows past the context length stay inside the
 // block and are masked when consumed.
-template <bool k16, int D>
+// kNT: non-temporal loads.
+template <bool k16, int D, bool kNT = false>
 __device__ __forceinline__ void issue_tile(TileRegs<k16, D>& r, const KvPool& a,
                                            int32_t phys, int32_t t, int32_t kvh, int lane,
                                            bool valid) {
+  constexpr int kAux = kNT ? kNonTemporal : 0;
   using Geo = Geometry<k16, D>;
   const int bs_log = a.log2_bs;
   const int32_t bs = 1 << bs_log;
@@ -92,8 +98,8 @@ __device__ __forceinline__ void issue_tile(TileRegs<k16, D>& r, const KvPool& a,
   const int32_t ko = (lane & 15) * Geo::kRowBytes + jr * 16;
 #pragma unroll
   for (int p = 0; p < Geo::kKPieces; ++p)
-    r.k[p] = __builtin_bit_cast(u32x4_t,
-                                __builtin_amdgcn_raw_buffer_load_b128(rk, ko + p * 64, 0, 0));
+    r.k[p] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, ko + p * 64, 0, kAux));
   const int32_t vo = (jr * 4) * Geo::kRowBytes + c16 * (Geo::kVWords * 4);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -102,14 +108,14 @@ __device__ __forceinline__ void issue_tile(TileRegs<k16, D>& r, const KvPool& a,
       if constexpr (Geo::kVWords >= 4) {
         const u32x4_t x = __builtin_bit_cast(
             u32x4_t,
-            __builtin_amdgcn_raw_buffer_load_b128(rv, vo + q * Geo::kRowBytes + h * 4, 0, 0));
+            __builtin_amdgcn_raw_buffer_load_b128(rv, vo + q * Geo::kRowBytes + h * 4, 0, kAux));
         r.v[q][h + 0] = x[0];
         r.v[q][h + 1] = x[1];
         r.v[q][h + 2] = x[2];
         r.v[q][h + 3] = x[3];
       } else {
         const uint2 x = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vo + q * Geo::kRowBytes, 0, 0));
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vo + q * Geo::kRowBytes, 0, kAux));
         r.v[q][0] = x.x;
         r.v[q][1] = x.y;
       }
@@ -126,7 +132,7 @@ __device__ __forceinline__ void issue_tile(TileRegs<k16, D>& r, const KvPool& a,
 // new_row >= 0: row new_row of the tile is read from nk / nv (the first byte
 // of the new token's K and V rows) instead of the pools (see
 // issue_tile_with_row).
-template <bool k16, int D>
+template <bool k16, int D, bool kNT = false>
 __device__ __forceinline__ void issue_tile_small(TileRegs<k16, D>& r, const KvPool& a,
                                                  int32_t phys_v, int32_t jl, int32_t t,
                                                  int32_t kvh, int32_t L, int nbt, int lane,
@@ -150,8 +156,12 @@ __device__ __forceinline__ void issue_tile_small(TileRegs<k16, D>& r, const KvPo
   // active.
   const char* kc = row_addr(lane & 15, a.k_cache);
   const char* kp = (c16 == new_row ? nk : kc) + jr * 16;
+  auto ld16 = [](const char* p) -> u32x4_t {
+    if constexpr (kNT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    else return *reinterpret_cast<const u32x4_t*>(p);
+  };
 #pragma unroll
-  for (int p = 0; p < Geo::kKPieces; ++p) r.k[p] = *reinterpret_cast<const u32x4_t*>(kp + p * 64);
+  for (int p = 0; p < Geo::kKPieces; ++p) r.k[p] = ld16(kp + p * 64);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const char* vc = row_addr(jr * 4 + q, a.v_cache);
@@ -159,15 +169,18 @@ __device__ __forceinline__ void issue_tile_small(TileRegs<k16, D>& r, const KvPo
 #pragma unroll
     for (int h = 0; h < Geo::kVWords; h += 4) {
       if constexpr (Geo::kVWords >= 4) {
-        u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp + h * 4);
+        const u32x4_t x = ld16(vp + h * 4);
         r.v[q][h + 0] = x[0];
         r.v[q][h + 1] = x[1];
         r.v[q][h + 2] = x[2];
         r.v[q][h + 3] = x[3];
       } else {
-        uint2 x = *reinterpret_cast<const uint2*>(vp);
-        r.v[q][0] = x.x;
-        r.v[q][1] = x.y;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 x;
+        if constexpr (kNT) x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp));
+        else x = *reinterpret_cast<const u32x2*>(vp);
+        r.v[q][0] = x[0];
+        r.v[q][1] = x[1];
       }
     }
   }

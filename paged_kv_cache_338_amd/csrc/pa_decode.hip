@@ -365,7 +365,7 @@ struct LdsPieces {
   int32_t flag[2];         // per published piece: 0 not last, 1 merge from L2, 2 at device scope
 };
 
-template <int E, int D, int GP, int NBUF, bool kSmall, bool kAppend>
+template <int E, int D, int GP, int NBUF, bool kSmall, bool kAppend, bool kNT>
 __global__ void __launch_bounds__(kWG)
 __attribute__((amdgpu_waves_per_eu(kSmall ? (((E != 0) || GP * D < 16 * 128) ? 2 : 1)
                                           : ((E != 0) ? 2 : 1))))
@@ -659,7 +659,7 @@ decode_kernel(DecodeArgs a) {
             const bool inA = u < bt.nA;
             const int32_t S1 = inA ? bt.A.S1 : bt.B.S1, L = inA ? bt.A.L : bt.B.L;
             const int32_t b = inA ? bt.A.b : bt.B.b;
-            issue_tile<BF16, D>(buf[u], a.pool(), ph[u], t, kvh, lane, u < bt.n);
+            issue_tile<BF16, D, kNT>(buf[u], a.pool(), ph[u], t, kvh, lane, u < bt.n);
             if (u < bt.n && bt.fa + u == S1 - 1) {  // uniform
               const int64_t src = ((int64_t)b * H_kv + kvh) * Geo::kRowBytes;
               pa::reload_new_row<BF16, D>(buf[u], (L - 1) & (kTile - 1),
@@ -668,7 +668,7 @@ decode_kernel(DecodeArgs a) {
             }
             continue;
           }
-          issue_tile<BF16, D>(buf[u], a.pool(), ph[u], t, kvh, lane, u < bt.n);
+          issue_tile<BF16, D, kNT>(buf[u], a.pool(), ph[u], t, kvh, lane, u < bt.n);
         }
         const Batch nx = next();
         batch_phys(nx, ph);
@@ -750,15 +750,15 @@ decode_kernel(DecodeArgs a) {
           if constexpr (kAppend) {
             if (j < n && t0 + jj == s.nt - 1) {  // uniform: the segment's last tile
               const int64_t src = ((int64_t)s.b * H_kv + s.kvh) * Geo::kRowBytes;
-              issue_tile_small<BF16, D>(r, a.pool(), dA, jj - (c << tpc_log), t0 + jj, s.kvh, s.L,
-                                        nbt, lane, (s.L - 1) & (kTile - 1),
+              issue_tile_small<BF16, D, kNT>(r, a.pool(), dA, jj - (c << tpc_log), t0 + jj, s.kvh,
+                                             s.L, nbt, lane, (s.L - 1) & (kTile - 1),
                                         reinterpret_cast<const char*>(a.new_k) + src,
                                         reinterpret_cast<const char*>(a.new_v) + src);
               return;
             }
           }
-          issue_tile_small<BF16, D>(r, a.pool(), dA, jj - (c << tpc_log), t0 + jj, s.kvh, s.L, nbt,
-                                    lane);
+          issue_tile_small<BF16, D, kNT>(r, a.pool(), dA, jj - (c << tpc_log), t0 + jj, s.kvh, s.L,
+                                         nbt, lane);
         };
         pa::static_for<0, NBUF - 1>([&](auto U) { issue(buf[decltype(U)::value], decltype(U)::value); });
         for (int32_t j0 = 0; j0 < n; j0 += NBUF) {
@@ -1093,10 +1093,16 @@ size_t lds_bytes(int32_t B) {
 template <int E, int D, int GP>
 pa_status launch(const DecodeArgs& a, int wgs, hipStream_t s) {
   constexpr int NB = kNbuf<(E != 0), D, GP, false>, NBA = kNbuf<(E != 0), D, GP, true>;
-  auto kern = a.new_k ? (a.log2_bs >= 4 ? decode_kernel<E, D, GP, NBA, false, true>
-                                        : decode_kernel<E, D, GP, NBA, true, true>)
-                      : (a.log2_bs >= 4 ? decode_kernel<E, D, GP, NB, false, false>
-                                        : decode_kernel<E, D, GP, NB, true, false>);
+  // K/V loads non-temporal unless the caller expects shared blocks.
+  const bool nt = pa::tuning(PA_TUNE_DECODE_KV_CACHED) == 0;
+  auto pick = [&](auto kNTc) {
+    constexpr bool kNT = decltype(kNTc)::value;
+    return a.new_k ? (a.log2_bs >= 4 ? decode_kernel<E, D, GP, NBA, false, true, kNT>
+                                     : decode_kernel<E, D, GP, NBA, true, true, kNT>)
+                   : (a.log2_bs >= 4 ? decode_kernel<E, D, GP, NB, false, false, kNT>
+                                     : decode_kernel<E, D, GP, NB, true, false, kNT>);
+  };
+  auto kern = nt ? pick(std::true_type{}) : pick(std::false_type{});
   const size_t lds = lds_bytes<D, GP>(a.B);
   if (lds > kMaxLds)
     return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: %d sequences need %zu bytes of LDS (> %zu)",

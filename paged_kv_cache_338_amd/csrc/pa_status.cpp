@@ -10,7 +10,7 @@
 namespace {
 thread_local std::string g_last_error;
 // Tuning knobs, indexed by pa_tuning_key; 0 = the library's own choice.
-std::atomic<int32_t> g_tuning[3];
+std::atomic<int32_t> g_tuning[4];
 }
 
 namespace pa {
@@ -33,7 +33,7 @@ int ilog2_exact(int32_t x) {
 }
 
 int32_t tuning(pa_tuning_key key) {
-  return key >= 1 && key <= 2 ? g_tuning[key].load(std::memory_order_relaxed) : 0;
+  return key >= 1 && key <= 3 ? g_tuning[key].load(std::memory_order_relaxed) : 0;
 }
 
 pa_status check_desc(const pa_cache_desc* desc) {
@@ -68,6 +68,10 @@ pa_status pa_set_tuning(pa_tuning_key key, int32_t value) {
       if (value < 0 || value > (1 << 20))
         return pa::fail(PA_ERR_INVALID_ARGUMENT, "prefill key tiles %d not in [0, 2^20]", value);
       break;
+    case PA_TUNE_DECODE_KV_CACHED:
+      if (value < 0 || value > 1)
+        return pa::fail(PA_ERR_INVALID_ARGUMENT, "decode KV cached %d not 0 or 1", value);
+      break;
     default:
       return pa::fail(PA_ERR_INVALID_ARGUMENT, "unknown tuning key %d", key);
   }
@@ -77,7 +81,8 @@ pa_status pa_set_tuning(pa_tuning_key key, int32_t value) {
 
 pa_status pa_get_tuning(pa_tuning_key key, int32_t* value) {
   if (!value) return pa::fail(PA_ERR_INVALID_ARGUMENT, "value is NULL");
-  if (key != PA_TUNE_DECODE_WORKGROUPS && key != PA_TUNE_PREFILL_KEY_TILES)
+  if (key != PA_TUNE_DECODE_WORKGROUPS && key != PA_TUNE_PREFILL_KEY_TILES &&
+      key != PA_TUNE_DECODE_KV_CACHED)
     return pa::fail(PA_ERR_INVALID_ARGUMENT, "unknown tuning key %d", key);
   *value = pa::tuning(key);
   return PA_OK;

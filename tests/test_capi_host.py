@@ -534,3 +534,29 @@ def test_prefix_pins_on_c_allocator():
 
     for pin in tp.PREFIX_PINS:
         pin(C)
+
+
+def test_tuning_knobs_validate_and_round_trip():
+    """pa_set_tuning / pa_get_tuning: every key takes 0 (the library's choice)
+    and its documented range, rejects values outside it and unknown keys."""
+    lib = pa.load_library()
+    ranges = {pa.PA_TUNE_DECODE_WORKGROUPS: (1024, 1025), pa.PA_TUNE_PREFILL_KEY_TILES: (1 << 20, (1 << 20) + 1),
+              pa.PA_TUNE_DECODE_KV_CACHED: (1, 2)}
+    for key, (hi, bad) in ranges.items():
+        old = pa.pa_get_tuning(key)
+        try:
+            for v in (0, 1, hi):
+                pa.pa_set_tuning(key, v)
+                assert pa.pa_get_tuning(key) == v
+            for v in (-1, bad):
+                assert lib.pa_set_tuning(key, v) == pa.PA_ERR_INVALID_ARGUMENT
+                assert pa.pa_get_tuning(key) == hi  # unchanged by a rejected value
+        finally:
+            pa.pa_set_tuning(key, old)
+    for key in (0, 4, -3):
+        assert lib.pa_set_tuning(key, 0) == pa.PA_ERR_INVALID_ARGUMENT
+        v = ctypes.c_int32(7)
+        assert lib.pa_get_tuning(key, ctypes.byref(v)) == pa.PA_ERR_INVALID_ARGUMENT
+    with pa.tuning(pa.PA_TUNE_DECODE_KV_CACHED, 1):
+        assert pa.pa_get_tuning(pa.PA_TUNE_DECODE_KV_CACHED) == 1
+    assert pa.pa_get_tuning(pa.PA_TUNE_DECODE_KV_CACHED) == 0

@@ -187,6 +187,33 @@ def test_shapes(shape):
     assert_close(w, gc.decode(tables=wide, lens=lo), oc.decode())
 
 
+@pytest.mark.parametrize("case", ["llama", "prefix2056", "bs4", "f32_g8", "f16_bs8"])
+def test_kv_load_policy_does_not_change_the_result(case):
+    """pa_decode with non-temporal K/V loads (the default) and with cached
+    loads (PA_TUNE_DECODE_KV_CACHED = 1): the same kernel arithmetic, so the
+    outputs are bit-identical, and both match the oracle."""
+    import paged_kv_cache_338_amd as pa
+    if case == "llama":
+        w = W.llama3_8b_decode()
+    elif case == "prefix2056":
+        w = W.prefix_sharing(prefix_len=2056)
+    elif case == "bs4":
+        w = _small(41, [3, 4, 5, 77, 300], 4, 2, 128, 4, "bf16")
+    elif case == "f32_g8":
+        w = _small(42, [1, 16, 17, 250], 8, 1, 128, 16, "f32")
+    else:
+        w = _small(43, [5, 130, 64], 8, 1, 64, 8, "f16")
+    oc, gc = run_both(w)
+    want = oc.decode()
+    outs = []
+    for cached in (0, 1):
+        with pa.tuning(pa.PA_TUNE_DECODE_KV_CACHED, cached):
+            out = gc.decode()
+        assert_close(w, out, want)
+        outs.append(_gd().to_numpy(out, w.dtype))
+    assert np.array_equal(outs[0], outs[1])
+
+
 def _direct_case(seed, lens, H_kv, G, D, bs, dtype):
     """Pools, tables and queries built directly: each sequence's blocks a
     shuffled slice of the pool, only its own token slots hold values, every
