@@ -342,6 +342,7 @@ def decode_floor(kpool, vpool, tables_np, lens_np, w, reps, wgs=256):
         kpool[l].data_ptr(), vpool[l].data_ptr(), per_pool, wgs, magic, sink.data_ptr(), h)))
     empty_us = time_graph(lambda l, h: check(lib.pa_floor_empty(wgs, h)))
     return {"tiles": n, "tile_bytes_each_of_k_and_v": tile, "bytes_read": 2 * n * tile,
+            "loads": "16-byte non-temporal, as the decode's K/V loads",
             "workgroups": wgs, "read_tiles_us": round(tiles_us, 3),
             "read_contiguous_us": round(contig_us, 3), "empty_launch_us": round(empty_us, 3),
             "timing": f"{reps} replays of a graph of {nl} launches, one per layer pool"}

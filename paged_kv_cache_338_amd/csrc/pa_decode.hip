@@ -363,6 +363,7 @@ struct LdsPieces {
   float l[kSlots][GP];
   int4 seg[kSlots];        // S0, S1, b | kvh << 16 (kvh < 2^15), valid: one 16-byte read
   int32_t flag[2];         // per published piece: 0 not last, 1 merge from L2, 2 at device scope
+  int32_t la[2], n[2];     // per published piece: its segment's first contributor and count
 };
 
 template <int E, int D, int GP, int NBUF, bool kSmall, bool kAppend, bool kNT>
@@ -891,15 +892,15 @@ decode_kernel(DecodeArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // Contributors of published run j: the logical workgroups la.. whose
-  // shares meet the segment, n of them.
-  auto first_of = [&](int32_t S0) { return share_of(S0, Tt, nwg); };
-  auto count_of = [&](int32_t S0, int32_t S1) {
-    return Tt >= nwg ? share_of(S1 - 1, Tt, nwg) - share_of(S0, Tt, nwg) + 1 : S1 - S0;
-  };
+  // shares meet the segment, n of them (one per tile when there are fewer
+  // tiles than workgroups).
   if (tid < pub_n) {
     const int32_t S0 = tid == 0 ? p0S0 : p1S0, S1 = tid == 0 ? p0S1 : p1S1;
     const int32_t bh = tid == 0 ? p0bh : p1bh, b = bh & 0xFFFF, kvh = bh >> 16;
-    const int32_t n = count_of(S0, S1);
+    const int32_t la = share_of(S0, Tt, nwg);
+    const int32_t n = Tt >= nwg ? share_of(S1 - 1, Tt, nwg) - la + 1 : S1 - S0;
+    P.la[tid] = la;  // for the merge, should this workgroup be last
+    P.n[tid] = n;
     // Arrival: the count in bits 0-15, the sum of the contributors' XCD
     // numbers x in bits 16-31 and of x^2 in bits 32-47 (n <= 1024, x <= 7).
     // The n contributors ran on one XCD iff n * sum(x^2) = sum(x)^2, and on
@@ -940,7 +941,7 @@ decode_kernel(DecodeArgs a) {
     const int32_t S0 = j ? p1S0 : p0S0, S1 = j ? p1S1 : p0S1;
     const int32_t bh = j ? p1bh : p0bh, b = bh & 0xFFFF, kvh = bh >> 16;
     const bool device_scope = (j ? f1 : f0) == 2;
-    const int32_t la = share_of(S0, Tt, nwg), n = count_of(S0, S1);
+    const int32_t la = P.la[j], n = P.n[j];
     // Piece slot of contributor i: the first holds the segment's start
     // (slot 1 of its workgroup), every later one began before its share.
     auto piece = [&](int32_t i) {

@@ -10,9 +10,10 @@
 //   * pa_floor_read_contiguous: read the same number of bytes as one
 //     contiguous range per pool;
 //   * pa_floor_empty: a launch that does nothing (the per-launch cost).
-// Loaded words are folded by XOR into a value stored only when it equals a
-// caller-chosen number, so the loads cannot be dropped and almost nothing is
-// written.  Every entry point returns a hipError_t value.
+// Loads are non-temporal, as the decode's K/V loads.  Loaded words are
+// folded by XOR into a value stored only when it equals a caller-chosen
+// number, so the loads cannot be dropped and almost nothing is written.
+// Every entry point returns a hipError_t value.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,7 +26,10 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTileBytes = 4096;  // 16 tokens x 128 values x 2 bytes
 
-__device__ inline u32x4 ld16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+// Non-temporal, as the decode's K/V loads: each byte is read once per launch.
+__device__ inline u32x4 ld16(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 __device__ inline void sink_if(u32x4 acc, uint32_t magic, uint32_t* sink) {
   const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
