@@ -1039,8 +1039,13 @@ def main():
     outs = [torch.empty_like(q) for _ in range(nl)]
     ws = pa.decode_workspace(kpool[0], B, H_q, maxb)
     tables_np, lens_np = alloc.build_block_tables(w.seq_ids, maxb)
-    tables_d = torch.from_numpy(tables_np).to(dev)
-    lens_d = torch.from_numpy(lens_np).to(dev)
+    # The tables and the lengths side by side in one device buffer, so that
+    # each step uploads its metadata with one copy.
+    meta_d = torch.empty(B * maxb + B, dtype=torch.int32, device=dev)
+    tables_d = meta_d[:B * maxb].view(B, maxb)
+    lens_d = meta_d[B * maxb:]
+    tables_d.copy_(torch.from_numpy(tables_np))
+    lens_d.copy_(torch.from_numpy(lens_np))
     torch.cuda.synchronize()
     log("prefill done")
 
@@ -1109,10 +1114,12 @@ def main():
     new_k = to_dev(w.notes["new_k"], w.dtype, dev)
     new_v = to_dev(w.notes["new_v"], w.dtype, dev)
     pin = [dict(slots=torch.empty(B, dtype=torch.int64, pin_memory=True),
-                tables=torch.empty((B, maxb), dtype=torch.int32, pin_memory=True),
-                lens=torch.empty(B, dtype=torch.int32, pin_memory=True),
+                meta=torch.empty(B * maxb + B, dtype=torch.int32, pin_memory=True),
                 pairs=torch.empty((B, 2), dtype=torch.int32, pin_memory=True),
                 ev=torch.cuda.Event()) for _ in range(2)]
+    for buf in pin:  # the layout of meta_d
+        buf["tables"] = buf["meta"][:B * maxb].view(B, maxb)
+        buf["lens"] = buf["meta"][B * maxb:]
     pairs_d = torch.empty((B, 2), dtype=torch.int32, device=dev)
 
     def layer_calls():
@@ -1134,8 +1141,7 @@ def main():
             buf["pairs"].numpy()[:npairs] = p
         alloc.build_block_tables(seq_ids, maxb, tables_out=buf["tables"].numpy(),
                                  lens_out=buf["lens"].numpy())
-        tables_d.copy_(buf["tables"], non_blocking=True)
-        lens_d.copy_(buf["lens"], non_blocking=True)
+        meta_d.copy_(buf["meta"], non_blocking=True)
         if npairs:
             pairs_d[:npairs].copy_(buf["pairs"][:npairs], non_blocking=True)
         buf["ev"].record(stream)
